@@ -1,0 +1,159 @@
+/*
+ * mxfp4.h -- C ABI of the MXFP4 + block-Hadamard linear-layer library for AMD MI355X (gfx950).
+ *
+ * What it computes. The gist.science summary of "MXFP4 LLM pretraining" (Llama-3.1-8B on
+ * MI355X), section 방법론 (Methodology), runs all three GEMMs of a linear layer in MXFP4 -- the
+ * forward product (Fprop), the activation gradient (Dgrad) and the weight gradient (Wgrad) -- and
+ * stabilises them with a deterministic 16x16 or 32x32 Hadamard rotation of the operands before
+ * quantization (section "주요 기여 및 발견" §2: the deterministic H16 on the whole pipeline is
+ * what restores convergence; stochastic rounding is the other intervention it tries).
+ *
+ * MXFP4 here (OCP Microscaling Formats v1.0): blocks of 32 consecutive elements along the
+ * quantized axis share one E8M0 scale byte S (value 2^(S-127); 0xFF = NaN) and each element is an
+ * E2M1 code (sign bit 3, magnitude index into {0, .5, 1, 1.5, 2, 3, 4, 6}). Two codes per byte,
+ * the even element in the low nibble (molayo1419.me NVFP4 article, "주요 사실": two 4-bit values
+ * packed into one byte).
+ *
+ * Conventions fixed by this library (the pages leave them open):
+ *  - H_h is the unnormalised Sylvester Hadamard H[i][j] = (-1)^popcount(i&j), applied to each
+ *    aligned group of h consecutive elements along the quantized axis, as a binary32 fast
+ *    Walsh-Hadamard transform with strides 1, 2, 4, ... and pair update (u, w) -> (u+w, u-w).
+ *    Since H_h H_h^T = h I, GEMMs of rotated operands are scaled by alpha = 1/h.
+ *  - Scale byte: S = floor(log2(amax)) - 2 + 127 clamped to [0, 254]; 0xFF (and all codes 0)
+ *    when the block holds a NaN or infinity after rotation; 0 for an all-zero block.
+ *  - Nearest rounding: ties to the even code, saturation at 6; the sign bit follows the sign
+ *    of the rotated value, also for zero results.
+ *  - Stochastic rounding: |v| >= 6 saturates; otherwise rounds up to the next grid value iff
+ *    r < 2^32 (|v| - lo) / (hi - lo), r = word (i mod 4) of Philox4x32-10 (Salmon et al., SC'11)
+ *    with key (seed mod 2^32, seed >> 32) and counter (floor(i/4) mod 2^32, floor(i/4) >> 32,
+ *    stream, 0), where i = o * L + j is the element's position in the quantized output
+ *    (row o of the output, position j along the quantized axis of length L).
+ *
+ * Memory and execution conventions (every entry point):
+ *  - All tensor pointers are DEVICE pointers, row-major, owned by the caller. The library never
+ *    allocates, frees or retains them. `stream` is a hipStream_t passed as void* (NULL = the
+ *    default stream); work is enqueued asynchronously and the call returns before it finishes.
+ *  - Argument errors are detected before any launch: the call returns the error code, launches
+ *    nothing and leaves every output untouched. A failed launch returns MXFP4_ERR_LAUNCH.
+ *    Nothing aborts and nothing throws across this interface.
+ *  - No hidden state: calls are reentrant. Results are deterministic run to run (quantization
+ *    bit-exact; GEMMs accumulate in a fixed order, no atomics).
+ *  - The device current on the calling thread must be a gfx950 GPU (else MXFP4_ERR_DEVICE).
+ */
+#ifndef MXFP4_H_
+#define MXFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXFP4_ABI_VERSION 1
+
+typedef enum {
+    MXFP4_OK = 0,
+    MXFP4_ERR_NULL = 1,      /* a required pointer is NULL */
+    MXFP4_ERR_SHAPE = 2,     /* a size is negative, or a quantized / contraction length % 32 != 0 */
+    MXFP4_ERR_ARG = 3,       /* bad enum, hadamard not in {0,16,32}, ld smaller than the row */
+    MXFP4_ERR_ALIGN = 4,     /* pointer or leading dimension misaligned (see each call) */
+    MXFP4_ERR_WORKSPACE = 5, /* workspace smaller than mxfp4_linear_workspace_bytes() */
+    MXFP4_ERR_DEVICE = 6,    /* no current HIP device, or it is not gfx950 */
+    MXFP4_ERR_LAUNCH = 7     /* the HIP runtime reported a launch error */
+} mxfp4_status_t;
+
+typedef enum { MXFP4_IN_BF16 = 0, MXFP4_IN_F32 = 1 } mxfp4_dtype_t;
+
+typedef enum { MXFP4_RNE = 0, MXFP4_SR_PHILOX = 1 } mxfp4_rounding_t;
+
+typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
+
+/*
+ * mxfp4_quantize -- rotate then quantize a 2-D tensor to MXFP4.
+ *
+ * Defined by: the operand transform of the Methodology section (deterministic H16/H32 rotation,
+ * then MXFP4 with nearest or stochastic rounding), with the conventions above.
+ *
+ *   x        device, T[rows][cols] with row stride ldx elements; dtype bf16 or f32.
+ *   axis=1   quantize along each row (L = cols):   q[rows][ldq bytes, first cols/2 used],
+ *                                                  scales[rows][lds bytes, first cols/32 used].
+ *   axis=0   quantize along each column (L = rows) and write the quantized TRANSPOSE:
+ *                                                  q[cols][ldq], scales[cols][lds]
+ *            (the Wgrad token axis and the Dgrad weight operand).
+ *   hadamard 0 (no rotation), 16 or 32; rounding MXFP4_RNE or MXFP4_SR_PHILOX with (seed, stream).
+ *
+ * Requirements: rows, cols >= 0; L % 32 == 0; ldx >= cols; ldq >= L/2; lds >= L/32.
+ * Alignment: x 16-byte aligned and ldx * sizeof(element) a multiple of 16; q 16-byte aligned and
+ * ldq % 16 == 0. Empty tensors return MXFP4_OK without a launch.
+ */
+mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                              int64_t ldx, int axis, int hadamard, mxfp4_rounding_t rounding,
+                              uint64_t seed, uint32_t stream_id, uint8_t *q, int64_t ldq,
+                              uint8_t *scales, int64_t lds, void *stream);
+
+/*
+ * mxfp4_gemm -- block-scaled FP4 GEMM with FP32 accumulation and output.
+ *
+ * Defined by: the MXFP4 GEMMs of the Methodology section, run natively on the FP4 matrix cores.
+ *   c[m][n] = alpha * sum_k deq(A)[m][k] * deq(B)[n][k],  m < M, n < N, k < K,
+ * with A = (aq [M][lda bytes], as [M][ldas bytes]) and B = (bq [N][ldb], bs [N][ldbs]) both
+ * quantized along K (the layout mxfp4_quantize writes), deq(code, S) = e2m1(code) * 2^(S-127).
+ * Any 0xFF scale in the contributing blocks makes the output NaN.
+ * c is FP32 [M][ldc] (device). Requirements: M, N, K >= 0, K % 32 == 0, lda, ldb >= K/2 and
+ * multiples of 16, ldas, ldbs >= K/32, ldc >= N; aq, bq 16-byte aligned.
+ */
+mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
+                          const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
+                          int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,
+                          void *stream);
+
+/* Per-operand configuration of one linear-layer GEMM. */
+typedef struct {
+    int hadamard;              /* 0, 16 or 32: rotation along the GEMM's contraction axis */
+    mxfp4_rounding_t rnd_a;    /* rounding of the first operand (X, dY, dY^T) */
+    mxfp4_rounding_t rnd_b;    /* rounding of the second operand (W, W^T, X^T) */
+    uint64_t seed;             /* Philox key for stochastic rounding; stream 0 = first operand,
+                                  stream 1 = second operand */
+} mxfp4_linear_cfg_t;
+
+/*
+ * Workspace (device bytes) the linear calls need for the two quantized operands of `pass` at
+ * X[M][K], W[N][K], dY[M][N]. Returns 0 for invalid sizes.
+ */
+size_t mxfp4_linear_workspace_bytes(mxfp4_pass_t pass, int64_t M, int64_t K, int64_t N);
+
+/*
+ * The three GEMMs of a linear layer Y = X W^T (Methodology section: Fprop, Dgrad, Wgrad), each
+ * operand rotated along the GEMM's contraction axis and quantized to MXFP4, then multiplied on
+ * the FP4 matrix cores with FP32 accumulation; alpha = 1/h is applied in the epilogue.
+ *   fprop: y[M][N]  = X[M][K] . W[N][K]^T      (both quantized along K)
+ *   dgrad: dx[M][K] = dY[M][N] . W[N][K]       (dY along N; W along N, i.e. transposed)
+ *   wgrad: dw[N][K] = dY[M][N]^T . X[M][K]     (both along the token axis M, transposed)
+ * Inputs are bf16, dense row-major (leading dimension = row length), 16-byte aligned; outputs
+ * FP32 dense row-major. ws is a device buffer of at least mxfp4_linear_workspace_bytes() bytes,
+ * 256-byte aligned, used only during the enqueued work (do not reuse it before it finishes).
+ * The contraction length and every quantized length must be multiples of 32:
+ * fprop K, dgrad N, wgrad M.
+ */
+mxfp4_status_t mxfp4_linear_fprop(const void *x_bf16, const void *w_bf16, int64_t M, int64_t K,
+                                  int64_t N, const mxfp4_linear_cfg_t *cfg, void *ws,
+                                  size_t ws_bytes, float *y, void *stream);
+mxfp4_status_t mxfp4_linear_dgrad(const void *dy_bf16, const void *w_bf16, int64_t M, int64_t K,
+                                  int64_t N, const mxfp4_linear_cfg_t *cfg, void *ws,
+                                  size_t ws_bytes, float *dx, void *stream);
+mxfp4_status_t mxfp4_linear_wgrad(const void *dy_bf16, const void *x_bf16, int64_t M, int64_t K,
+                                  int64_t N, const mxfp4_linear_cfg_t *cfg, void *ws,
+                                  size_t ws_bytes, float *dw, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *mxfp4_status_string(mxfp4_status_t status);
+
+/* MXFP4_ABI_VERSION of the built library. */
+int mxfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H_ */

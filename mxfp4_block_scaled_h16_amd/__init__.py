@@ -1,0 +1,197 @@
+"""MXFP4 + block-Hadamard linear-layer GEMMs on AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libmxfp4.so`` (C ABI declared in ``include/mxfp4.h``). Every step of
+the hot path runs in the library's HIP kernels; this module only marshals arguments. PyTorch
+provides device memory (tensors) and the stream (the current HIP stream).
+
+The three GEMMs are those of the gist.science summary of "MXFP4 LLM pretraining", section 방법론
+(Methodology): Fprop Y = X W^T, Dgrad dX = dY W, Wgrad dW = dY^T X, each operand rotated by a
+deterministic block Hadamard (H16 / H32) along the GEMM's contraction axis and quantized to MXFP4.
+"""
+import ctypes
+import os
+
+import torch  # imported first: the library binds to the HIP runtime torch has loaded
+
+__all__ = [
+    "Mxfp4Error", "quantize", "gemm", "linear_fprop", "linear_dgrad", "linear_wgrad",
+    "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmxfp4.so")
+
+RNE, SR = 0, 1
+FPROP, DGRAD, WGRAD = 0, 1, 2
+BF16, F32 = 0, 1
+
+_lib = None
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, _status_string(status), status))
+
+
+class LinearCfg(ctypes.Structure):
+    _fields_ = [("hadamard", ctypes.c_int), ("rnd_a", ctypes.c_int), ("rnd_b", ctypes.c_int),
+                ("seed", ctypes.c_uint64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded C library; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("%s is missing: build it with `python -m mxfp4_block_scaled_h16_amd.build` "
+                          "(or __graft_entry__.build())" % _LIB_PATH)
+    L = ctypes.CDLL(_LIB_PATH)
+    i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
+    L.mxfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, u64, u32, vp, i64, vp, i64, vp]
+    L.mxfp4_quantize.restype = ci
+    L.mxfp4_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64, vp]
+    L.mxfp4_gemm.restype = ci
+    L.mxfp4_linear_workspace_bytes.argtypes = [ci, i64, i64, i64]
+    L.mxfp4_linear_workspace_bytes.restype = ctypes.c_size_t
+    for name in ("mxfp4_linear_fprop", "mxfp4_linear_dgrad", "mxfp4_linear_wgrad"):
+        f = getattr(L, name)
+        f.argtypes = [vp, vp, i64, i64, i64, ctypes.POINTER(LinearCfg), vp, ctypes.c_size_t, vp, vp]
+        f.restype = ci
+    L.mxfp4_status_string.argtypes = [ci]
+    L.mxfp4_status_string.restype = ctypes.c_char_p
+    L.mxfp4_abi_version.argtypes = []
+    L.mxfp4_abi_version.restype = ci
+    _lib = L
+    return L
+
+
+def _status_string(status):
+    try:
+        return lib().mxfp4_status_string(status).decode()
+    except Exception:  # noqa: BLE001 - only used to format an error message
+        return "status %d" % status
+
+
+def _check(status, where):
+    if status != 0:
+        raise Mxfp4Error(status, where)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _rounding(r):
+    if r in (RNE, "rne", "nearest"):
+        return RNE
+    if r in (SR, "sr", "stochastic"):
+        return SR
+    raise ValueError("rounding must be 'rne' or 'sr'")
+
+
+def _require_cuda(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a tensor on a HIP device" % name)
+
+
+def quantize(x, axis=1, hadamard=16, rounding="rne", seed=0, stream_id=0, q=None, scales=None,
+             stream=None):
+    """Rotate then quantize a 2-D bf16/f32 device tensor to MXFP4.
+
+    Returns (q uint8 [outer, L/2], scales uint8 [outer, L/32]); axis=0 gives the quantized
+    transpose (outer = columns).
+    """
+    _require_cuda(x, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    dtype = {torch.bfloat16: BF16, torch.float32: F32}.get(x.dtype)
+    if dtype is None:
+        raise TypeError("x must be bfloat16 or float32")
+    rows, cols = x.shape
+    L, outer = (cols, rows) if axis == 1 else (rows, cols)
+    if q is None:
+        q = torch.empty((outer, L // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((outer, L // 32), dtype=torch.uint8, device=x.device)
+    st = lib().mxfp4_quantize(x.data_ptr(), dtype, rows, cols, x.stride(0), axis, hadamard,
+                              _rounding(rounding), int(seed) & (2 ** 64 - 1), int(stream_id),
+                              q.data_ptr(), q.stride(0), scales.data_ptr(), scales.stride(0),
+                              _stream(stream))
+    _check(st, "mxfp4_quantize")
+    return q, scales
+
+
+def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None):
+    """c[m][n] = alpha * sum_k deq(A)[m][k] deq(B)[n][k] (FP32 [M, N])."""
+    for t, n in ((aq, "aq"), (as_, "as"), (bq, "bq"), (bs, "bs")):
+        _require_cuda(t, n)
+    M, K = aq.shape[0], aq.shape[1] * 2
+    N = bq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=aq.device)
+    st = lib().mxfp4_gemm(aq.data_ptr(), aq.stride(0), as_.data_ptr(), as_.stride(0), bq.data_ptr(),
+                          bq.stride(0), bs.data_ptr(), bs.stride(0), M, N, K, float(alpha),
+                          out.data_ptr(), out.stride(0), _stream(stream))
+    _check(st, "mxfp4_gemm")
+    return out
+
+
+def workspace_bytes(pass_, M, K, N) -> int:
+    return int(lib().mxfp4_linear_workspace_bytes(int(pass_), int(M), int(K), int(N)))
+
+
+def _linear(fn_name, pass_, a, b, M, K, N, out_shape, hadamard, rnd_a, rnd_b, seed, out, workspace,
+            stream):
+    _require_cuda(a, "first operand")
+    _require_cuda(b, "second operand")
+    for t in (a, b):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError("linear operands must be contiguous bfloat16")
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.float32, device=a.device)
+    need = workspace_bytes(pass_, M, K, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
+    cfg = LinearCfg(int(hadamard), _rounding(rnd_a), _rounding(rnd_b), int(seed) & (2 ** 64 - 1))
+    st = getattr(lib(), fn_name)(a.data_ptr(), b.data_ptr(), M, K, N, ctypes.byref(cfg),
+                                 workspace.data_ptr(), workspace.numel(), out.data_ptr(),
+                                 _stream(stream))
+    _check(st, fn_name)
+    return out
+
+
+def linear_fprop(x, w, hadamard=16, rnd_a="rne", rnd_b="rne", seed=0, out=None, workspace=None,
+                 stream=None):
+    """Y[M,N] = X[M,K] W[N,K]^T with both operands rotated and quantized along K."""
+    M, K = x.shape
+    N = w.shape[0]
+    return _linear("mxfp4_linear_fprop", FPROP, x, w, M, K, N, (M, N), hadamard, rnd_a, rnd_b,
+                   seed, out, workspace, stream)
+
+
+def linear_dgrad(dy, w, hadamard=16, rnd_a="rne", rnd_b="rne", seed=0, out=None, workspace=None,
+                 stream=None):
+    """dX[M,K] = dY[M,N] W[N,K] with both operands rotated and quantized along N."""
+    M, N = dy.shape
+    K = w.shape[1]
+    return _linear("mxfp4_linear_dgrad", DGRAD, dy, w, M, K, N, (M, K), hadamard, rnd_a, rnd_b,
+                   seed, out, workspace, stream)
+
+
+def linear_wgrad(dy, x, hadamard=16, rnd_a="rne", rnd_b="rne", seed=0, out=None, workspace=None,
+                 stream=None):
+    """dW[N,K] = dY[M,N]^T X[M,K] with both operands rotated and quantized along the tokens M."""
+    M, N = dy.shape
+    K = x.shape[1]
+    return _linear("mxfp4_linear_wgrad", WGRAD, dy, x, M, K, N, (N, K), hadamard, rnd_a, rnd_b,
+                   seed, out, workspace, stream)

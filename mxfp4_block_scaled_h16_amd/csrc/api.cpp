@@ -1,0 +1,249 @@
+// C-ABI entry points: argument validation, workspace carve-up and kernel dispatch.
+// Every argument check happens before the first HIP call, so an invalid call launches nothing,
+// touches no output and needs no device.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/mxfp4.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxBlocks = (int64_t)1 << 31;  // 32-element blocks per quantize launch
+constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+mxfp4_status_t check_device()
+{
+    // gfx950 check, cached per device ordinal: 0 = unknown, 1 = gfx950, 2 = other
+    static std::atomic<int> cache[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MXFP4_ERR_DEVICE;
+    if (dev < 64) {
+        const int known = cache[dev].load(std::memory_order_relaxed);
+        if (known) return known == 1 ? MXFP4_OK : MXFP4_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXFP4_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
+
+mxfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_LAUNCH; }
+
+// Validation of one quantize call; also used by the linear entry points.
+mxfp4_status_t check_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                              int64_t ldx, int axis, int hadamard, mxfp4_rounding_t rounding,
+                              const uint8_t *q, int64_t ldq, const uint8_t *scales, int64_t lds)
+{
+    if (dtype != MXFP4_IN_BF16 && dtype != MXFP4_IN_F32) return MXFP4_ERR_ARG;
+    if (axis != 0 && axis != 1) return MXFP4_ERR_ARG;
+    if (hadamard != 0 && hadamard != 16 && hadamard != 32) return MXFP4_ERR_ARG;
+    if (rounding != MXFP4_RNE && rounding != MXFP4_SR_PHILOX) return MXFP4_ERR_ARG;
+    if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return MXFP4_ERR_SHAPE;
+    const int64_t L = axis ? cols : rows;
+    const int64_t outer = axis ? rows : cols;
+    if (L % 32 != 0) return MXFP4_ERR_SHAPE;
+    if (outer > 0 && L / 32 > 0 && outer > kMaxBlocks / (L / 32)) return MXFP4_ERR_SHAPE;
+    if (ldx < cols || ldx < 1 || ldq < L / 2 || lds < L / 32) return MXFP4_ERR_ARG;
+    if (rows == 0 || cols == 0) return MXFP4_OK;
+    if (!x || !q || !scales) return MXFP4_ERR_NULL;
+    const int64_t esize = dtype == MXFP4_IN_F32 ? 4 : 2;
+    if (!aligned(x, 16) || (ldx * esize) % 16 != 0) return MXFP4_ERR_ALIGN;
+    if (!aligned(q, 16) || ldq % 16 != 0) return MXFP4_ERR_ALIGN;
+    return MXFP4_OK;
+}
+
+mxfp4_status_t check_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
+                          const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
+                          int64_t M, int64_t N, int64_t K, const float *c, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MXFP4_ERR_SHAPE;
+    if (K % 32 != 0) return MXFP4_ERR_SHAPE;
+    if (lda < K / 2 || ldb < K / 2 || ldas < K / 32 || ldbs < K / 32 || ldc < N || ldc < 1)
+        return MXFP4_ERR_ARG;
+    if (M == 0 || N == 0) return MXFP4_OK;
+    if (!c) return MXFP4_ERR_NULL;
+    if (K > 0 && (!aq || !as || !bq || !bs)) return MXFP4_ERR_NULL;
+    if (!aligned(aq, 16) || !aligned(bq, 16) || lda % 16 != 0 || ldb % 16 != 0) return MXFP4_ERR_ALIGN;
+    if (!aligned(c, 4)) return MXFP4_ERR_ALIGN;
+    return MXFP4_OK;
+}
+
+// Workspace layout of one linear call: A codes | A scales | B codes | B scales, each 256-aligned.
+struct OperandSpace {
+    int64_t outer, L;
+    size_t codes() const { return (size_t)outer * (size_t)(L / 2); }
+    size_t scales() const { return (size_t)outer * (size_t)(L / 32); }
+};
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t layout_bytes(const OperandSpace &a, const OperandSpace &b)
+{
+    return round256(a.codes()) + round256(a.scales()) + round256(b.codes()) + round256(b.scales());
+}
+
+bool pass_operands(mxfp4_pass_t pass, int64_t M, int64_t K, int64_t N, OperandSpace *a, OperandSpace *b)
+{
+    switch (pass) {
+    case MXFP4_FPROP: *a = {M, K}; *b = {N, K}; return true;   // X along K, W along K
+    case MXFP4_DGRAD: *a = {M, N}; *b = {K, N}; return true;   // dY along N, W^T along N
+    case MXFP4_WGRAD: *a = {N, M}; *b = {K, M}; return true;   // dY^T along M, X^T along M
+    }
+    return false;
+}
+
+struct LinearSpec {
+    const void *a_src; int64_t a_rows, a_cols; int a_axis;  // first operand tensor and its axis
+    const void *b_src; int64_t b_rows, b_cols; int b_axis;
+    int64_t out_rows, out_cols, kc;                          // GEMM output and contraction
+};
+
+mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, int64_t K, int64_t N,
+                          const mxfp4_linear_cfg_t *cfg, void *ws, size_t ws_bytes, float *out,
+                          void *stream)
+{
+    if (!cfg) return MXFP4_ERR_NULL;
+    if (M < 0 || K < 0 || N < 0 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return MXFP4_ERR_SHAPE;
+    if (cfg->hadamard != 0 && cfg->hadamard != 16 && cfg->hadamard != 32) return MXFP4_ERR_ARG;
+    if ((cfg->rnd_a != MXFP4_RNE && cfg->rnd_a != MXFP4_SR_PHILOX) ||
+        (cfg->rnd_b != MXFP4_RNE && cfg->rnd_b != MXFP4_SR_PHILOX))
+        return MXFP4_ERR_ARG;
+    if (sp.kc % 32 != 0) return MXFP4_ERR_SHAPE;
+    OperandSpace a, b;
+    pass_operands(pass, M, K, N, &a, &b);
+    if (a.outer > 0 && a.L / 32 > 0 && (a.outer > kMaxBlocks / (a.L / 32) || b.outer > kMaxBlocks / (a.L / 32)))
+        return MXFP4_ERR_SHAPE;
+    if (sp.out_rows == 0 || sp.out_cols == 0) return MXFP4_OK;
+    if (!out) return MXFP4_ERR_NULL;
+    if (!aligned(out, 4)) return MXFP4_ERR_ALIGN;
+    const float alpha = cfg->hadamard ? 1.0f / (float)cfg->hadamard : 1.0f;
+    if (sp.kc == 0) {
+        // empty contraction: the product is all zeros
+        if (mxfp4_status_t st = check_device()) return st;
+        return from_hip(mx::launch_fill_zero(out, sp.out_rows, sp.out_cols, sp.out_cols,
+                                             (hipStream_t)stream));
+    }
+    if (!sp.a_src || !sp.b_src) return MXFP4_ERR_NULL;
+    if (!aligned(sp.a_src, 16) || !aligned(sp.b_src, 16)) return MXFP4_ERR_ALIGN;
+    if ((sp.a_cols * 2) % 16 != 0 || (sp.b_cols * 2) % 16 != 0) return MXFP4_ERR_ALIGN;
+    const size_t need = layout_bytes(a, b);
+    if (!ws || ws_bytes < need) return MXFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return MXFP4_ERR_ALIGN;
+    if (mxfp4_status_t st = check_device()) return st;
+
+    uint8_t *p = static_cast<uint8_t *>(ws);
+    uint8_t *aq = p;
+    uint8_t *as = aq + round256(a.codes());
+    uint8_t *bq = as + round256(a.scales());
+    uint8_t *bs = bq + round256(b.codes());
+    hipStream_t s = (hipStream_t)stream;
+    auto quant = [&](const void *src, int64_t rows, int64_t cols, int axis, mxfp4_rounding_t rnd,
+                     uint32_t sid, uint8_t *q, uint8_t *sc, int64_t L) {
+        if (axis == 1)
+            return mx::launch_quantize_rows(src, false, rows, cols, cols, cfg->hadamard,
+                                            rnd == MXFP4_SR_PHILOX, cfg->seed, sid, q, L / 2, sc,
+                                            L / 32, s);
+        return mx::launch_quantize_cols(src, false, rows, cols, cols, cfg->hadamard,
+                                        rnd == MXFP4_SR_PHILOX, cfg->seed, sid, q, L / 2, sc, L / 32, s);
+    };
+    hipError_t e = quant(sp.a_src, sp.a_rows, sp.a_cols, sp.a_axis, cfg->rnd_a, 0u, aq, as, a.L);
+    if (e == hipSuccess) e = quant(sp.b_src, sp.b_rows, sp.b_cols, sp.b_axis, cfg->rnd_b, 1u, bq, bs, b.L);
+    if (e == hipSuccess)
+        e = mx::launch_gemm(aq, a.L / 2, as, a.L / 32, bq, b.L / 2, bs, b.L / 32, sp.out_rows,
+                            sp.out_cols, sp.kc, alpha, out, sp.out_cols, s);
+    return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                              int64_t ldx, int axis, int hadamard, mxfp4_rounding_t rounding,
+                              uint64_t seed, uint32_t stream_id, uint8_t *q, int64_t ldq,
+                              uint8_t *scales, int64_t lds, void *stream)
+{
+    mxfp4_status_t st = check_quantize(x, dtype, rows, cols, ldx, axis, hadamard, rounding, q, ldq,
+                                       scales, lds);
+    if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    const bool f32 = dtype == MXFP4_IN_F32;
+    const bool sr = rounding == MXFP4_SR_PHILOX;
+    hipError_t e = axis == 1
+        ? mx::launch_quantize_rows(x, f32, rows, cols, ldx, hadamard, sr, seed, stream_id, q, ldq,
+                                   scales, lds, (hipStream_t)stream)
+        : mx::launch_quantize_cols(x, f32, rows, cols, ldx, hadamard, sr, seed, stream_id, q, ldq,
+                                   scales, lds, (hipStream_t)stream);
+    return from_hip(e);
+}
+
+mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
+                          const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
+                          int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,
+                          void *stream)
+{
+    mxfp4_status_t st = check_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, c, ldc);
+    if (st != MXFP4_OK || M == 0 || N == 0) return st;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    if (K == 0) {
+        // empty contraction: the product is all zeros
+        return from_hip(mx::launch_fill_zero(c, M, N, ldc, (hipStream_t)stream));
+    }
+    return from_hip(mx::launch_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, alpha, c, ldc,
+                                    (hipStream_t)stream));
+}
+
+size_t mxfp4_linear_workspace_bytes(mxfp4_pass_t pass, int64_t M, int64_t K, int64_t N)
+{
+    if (M < 0 || K < 0 || N < 0 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
+    OperandSpace a, b;
+    if (!pass_operands(pass, M, K, N, &a, &b)) return 0;
+    return layout_bytes(a, b);
+}
+
+mxfp4_status_t mxfp4_linear_fprop(const void *x_bf16, const void *w_bf16, int64_t M, int64_t K,
+                                  int64_t N, const mxfp4_linear_cfg_t *cfg, void *ws,
+                                  size_t ws_bytes, float *y, void *stream)
+{
+    LinearSpec sp{x_bf16, M, K, 1, w_bf16, N, K, 1, M, N, K};
+    return run_linear(sp, MXFP4_FPROP, M, K, N, cfg, ws, ws_bytes, y, stream);
+}
+
+mxfp4_status_t mxfp4_linear_dgrad(const void *dy_bf16, const void *w_bf16, int64_t M, int64_t K,
+                                  int64_t N, const mxfp4_linear_cfg_t *cfg, void *ws,
+                                  size_t ws_bytes, float *dx, void *stream)
+{
+    LinearSpec sp{dy_bf16, M, N, 1, w_bf16, N, K, 0, M, K, N};
+    return run_linear(sp, MXFP4_DGRAD, M, K, N, cfg, ws, ws_bytes, dx, stream);
+}
+
+mxfp4_status_t mxfp4_linear_wgrad(const void *dy_bf16, const void *x_bf16, int64_t M, int64_t K,
+                                  int64_t N, const mxfp4_linear_cfg_t *cfg, void *ws,
+                                  size_t ws_bytes, float *dw, void *stream)
+{
+    LinearSpec sp{dy_bf16, M, N, 0, x_bf16, M, K, 0, N, K, M};
+    return run_linear(sp, MXFP4_WGRAD, M, K, N, cfg, ws, ws_bytes, dw, stream);
+}
+
+const char *mxfp4_status_string(mxfp4_status_t status)
+{
+    switch (status) {
+    case MXFP4_OK: return "ok";
+    case MXFP4_ERR_NULL: return "a required pointer is NULL";
+    case MXFP4_ERR_SHAPE: return "invalid shape (negative size, length not a multiple of 32, or too large)";
+    case MXFP4_ERR_ARG: return "invalid argument (enum, hadamard size or leading dimension)";
+    case MXFP4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case MXFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXFP4_ERR_DEVICE: return "no current gfx950 device";
+    case MXFP4_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int mxfp4_abi_version(void) { return MXFP4_ABI_VERSION; }
+
+}  // extern "C"

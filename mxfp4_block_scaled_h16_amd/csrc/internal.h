@@ -1,0 +1,40 @@
+// Launchers shared by the C-ABI entry points (not part of the public interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// Arguments are validated by the caller; these only pick a kernel and enqueue it.
+hipError_t launch_quantize_rows(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
+                                int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
+                                uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
+                                hipStream_t stream);
+
+hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
+                                int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
+                                uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
+                                hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
+                       const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs, int64_t M,
+                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, hipStream_t stream);
+
+// c[m][n] = 0 for m < M, n < N (a kernel, not a memset, so it is safe inside captured graphs).
+hipError_t launch_fill_zero(float *c, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);
+
+// Launch a kernel through hipLaunchKernel so the runtime's error comes back directly.
+template <typename... Params, typename... Args>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t shared, hipStream_t stream,
+                  Args... args)
+{
+    static_assert(sizeof...(Params) == sizeof...(Args), "argument count");
+    auto pack = [&](auto... typed) {
+        void *argv[] = {(void *)&typed...};
+        return hipLaunchKernel((const void *)kernel, grid, block, argv, shared, stream);
+    };
+    return pack(static_cast<Params>(args)...);
+}
+
+}  // namespace mx

@@ -1,0 +1,200 @@
+// Device-side building blocks of the MXFP4 quantizers (gfx950).
+//
+// Format: OCP Microscaling Formats v1.0 MXFP4 -- 32-element blocks, one E8M0 scale byte per
+// block, E2M1 elements {0, .5, 1, 1.5, 2, 3, 4, 6} with a sign bit, two per byte (even element in
+// the low nibble). The rotation is the deterministic block Hadamard of the gist.science summary of
+// "MXFP4 LLM pretraining", section 방법론 (Methodology, H16 / H32), applied before quantization.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------- input widening --
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------- block Hadamard --
+// Unnormalised Sylvester transform of n values held in registers, binary32, strides 1, 2, 4, ...,
+// pair update (u, w) -> (u + w, u - w). The upper element is always u - w (never -(w - u)) so
+// signed zeros come out the same in every implementation of this order.
+template <int N>
+__device__ __forceinline__ void fwht_regs(float *v)
+{
+#pragma unroll
+    for (int s = 1; s < N; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if ((i & s) == 0) {
+                const float u = v[i], w = v[i + s];
+                v[i] = u + w;
+                v[i + s] = u - w;
+            }
+        }
+    }
+}
+
+// Rotate 32 values that form one MX block: H in {0, 16, 32}.
+template <int H>
+__device__ __forceinline__ void rotate_block(float *v)
+{
+    if constexpr (H == 16) {
+        fwht_regs<16>(v);
+        fwht_regs<16>(v + 16);
+    } else if constexpr (H == 32) {
+        fwht_regs<32>(v);
+    }
+}
+
+// ---------------------------------------------------------------------------- scale -----------
+// |x| as an unsigned bit pattern orders like |x|, with NaN above +inf.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// E8M0 byte from the block's largest |value| bit pattern: biased exponent E of amax gives
+// floor(log2 amax) = E - 127, so the shared exponent E - 127 - 2 is the byte E - 2 (clamped at 0).
+__device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits)
+{
+    if (amax_bits >= 0x7F800000u) return 0xFFu;
+    const uint32_t e = amax_bits >> 23;
+    return e > 2u ? e - 2u : 0u;
+}
+
+// 2^(127 - S) as binary32 for S <= 252 (exponent field 254 - S lies in [2, 254]).
+__device__ __forceinline__ float e8m0_reciprocal(uint32_t s)
+{
+    const uint32_t sc = s < 252u ? s : 252u;
+    return __uint_as_float((254u - sc) << 23);
+}
+
+// ---------------------------------------------------------------------------- E2M1 encode -----
+// Nearest-even E2M1 magnitude index of a >= 0 (a < 8 after scaling). Adding 1.5 * 2^23 * q
+// rounds a to a multiple of the grid step q in IEEE nearest-even, and the integer difference of
+// the sums' bit patterns counts those multiples; the low bit of that count is the code's mantissa
+// bit, so IEEE ties-to-even is the E2M1 ties-to-even. Saturates at index 7 (value 6).
+__device__ __forceinline__ uint32_t e2m1_nearest(float a)
+{
+    float bias;
+    uint32_t first;
+    if (a < 2.0f) {            // step 0.5: indices 0..4
+        bias = 6291456.0f;     // 1.5 * 2^22
+        first = 0u;
+    } else if (a < 4.0f) {    // step 1: values 2, 3, 4 -> indices 4, 5, 6
+        bias = 12582912.0f;    // 1.5 * 2^23
+        first = 2u;
+    } else {                   // step 2: values 4, 6, 8 -> indices 6, 7, (8 -> 7)
+        bias = 25165824.0f;    // 1.5 * 2^24
+        first = 4u;
+    }
+    const uint32_t k = __float_as_uint(a + bias) - __float_as_uint(bias) + first;
+    return k < 7u ? k : 7u;
+}
+
+// Stochastic E2M1 magnitude index of a >= 0 with random word r: saturate at 6, else round up to
+// the next grid value iff r < 2^32 * (fractional position of a between its two grid neighbours).
+// For integer r, r < t is r < ceil(t); every product below is exact in binary32.
+__device__ __forceinline__ uint32_t e2m1_stochastic(float a, uint32_t r)
+{
+    if (!(a < 6.0f)) return 7u;
+    float inv_step;
+    uint32_t first;
+    if (a < 2.0f) {
+        inv_step = 2.0f;
+        first = 0u;
+    } else if (a < 4.0f) {
+        inv_step = 1.0f;
+        first = 2u;
+    } else {
+        inv_step = 0.5f;
+        first = 4u;
+    }
+    const float t = a * inv_step;
+    const float lo = floorf(t);
+    const float frac = t - lo;
+    const uint32_t threshold = (uint32_t)ceilf(frac * 4294967296.0f);
+    return (uint32_t)lo + first + (r < threshold ? 1u : 0u);
+}
+
+// Sign of a binary32 value as the E2M1 sign bit (bit 3).
+__device__ __forceinline__ uint32_t sign_nibble(float y) { return (__float_as_uint(y) >> 28) & 8u; }
+
+// ---------------------------------------------------------------------------- Philox4x32-10 --
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten rounds;
+// each multiplies words 0 and 2 by fixed odd constants, swaps the halves of the products in and
+// mixes in the other words and the round key; the key advances by fixed Weyl increments.
+struct Philox4 {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p = (uint64_t)0xD2511F53u * c0;
+        const uint64_t q = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(q >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)q;
+        c3 = (uint32_t)p;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    Philox4 r;
+    r.w[0] = c0;
+    r.w[1] = c1;
+    r.w[2] = c2;
+    r.w[3] = c3;
+    return r;
+}
+
+// ---------------------------------------------------------------------------- one block -------
+// Encode 32 rotated values into four words of codes (8 codes per word, even element low) and
+// return the scale byte. index0 = position of v[0] in the quantized output (o * L + j); it is a
+// multiple of 32, so the block uses exactly 8 Philox counters.
+template <bool SR>
+__device__ __forceinline__ uint32_t encode_block(const float *v, uint32_t *words, uint64_t index0,
+                                                 uint32_t key0, uint32_t key1, uint32_t stream_id)
+{
+    uint32_t amax = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[i]));
+    const uint32_t s = e8m0_from_amax_bits(amax);
+    const float mul = e8m0_reciprocal(s);
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+        uint32_t word = 0u;
+        if constexpr (SR) {
+            const uint64_t ctr = (index0 >> 2) + (uint64_t)(2 * wd);
+            const Philox4 r0 = philox4x32_10((uint32_t)ctr, (uint32_t)(ctr >> 32), stream_id, 0u, key0, key1);
+            const uint64_t ctr1 = ctr + 1;
+            const Philox4 r1 = philox4x32_10((uint32_t)ctr1, (uint32_t)(ctr1 >> 32), stream_id, 0u, key0, key1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y = v[8 * wd + e];
+                const uint32_t rnd = e < 4 ? r0.w[e] : r1.w[e - 4];
+                const uint32_t code = e2m1_stochastic(fabsf(y * mul), rnd) | sign_nibble(y);
+                word |= code << (4 * e);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y = v[8 * wd + e];
+                const uint32_t code = e2m1_nearest(fabsf(y * mul)) | sign_nibble(y);
+                word |= code << (4 * e);
+            }
+        }
+        words[wd] = (s == 0xFFu) ? 0u : word;
+    }
+    return s;
+}
+
+}  // namespace mx

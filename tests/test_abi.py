@@ -1,0 +1,111 @@
+"""C-ABI library checks that need no GPU: it loads, exports every declared symbol, and its
+host-side logic (argument validation, workspace sizing, status strings) behaves as declared.
+No call here reaches a kernel launch: invalid arguments are rejected before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import mxfp4_block_scaled_h16_amd as mx
+    return mx.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for expected in ("mxfp4_quantize", "mxfp4_gemm", "mxfp4_linear_fprop", "mxfp4_linear_dgrad",
+                     "mxfp4_linear_wgrad", "mxfp4_linear_workspace_bytes", "mxfp4_status_string",
+                     "mxfp4_abi_version"):
+        assert expected in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.mxfp4_abi_version() == 1
+    for st in range(8):
+        assert L.mxfp4_status_string(st)
+    assert L.mxfp4_status_string(0) == b"ok"
+    assert b"unknown" in L.mxfp4_status_string(99)
+
+
+def test_workspace_bytes(L):
+    import mxfp4_block_scaled_h16_amd as mx
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    M, K, N = 8192, 4096, 6144
+    assert mx.workspace_bytes(mx.FPROP, M, K, N) == r(M * K // 2) + r(M * K // 32) + r(N * K // 2) + r(N * K // 32)
+    assert mx.workspace_bytes(mx.DGRAD, M, K, N) == r(M * N // 2) + r(M * N // 32) + r(K * N // 2) + r(K * N // 32)
+    assert mx.workspace_bytes(mx.WGRAD, M, K, N) == r(N * M // 2) + r(N * M // 32) + r(K * M // 2) + r(K * M // 32)
+    assert mx.workspace_bytes(mx.FPROP, -1, K, N) == 0
+    assert mx.workspace_bytes(7, M, K, N) == 0
+
+
+def _q(L, x=1 << 12, dtype=0, rows=64, cols=64, ldx=64, axis=1, h=16, rnd=0, q=1 << 12, ldq=32,
+       s=1 << 12, lds=2):
+    return L.mxfp4_quantize(x, dtype, rows, cols, ldx, axis, h, rnd, 0, 0, q, ldq, s, lds, None)
+
+
+def test_quantize_argument_errors(L):
+    assert _q(L, cols=48, ldx=48, ldq=24) == 2            # length not a multiple of 32
+    assert _q(L, rows=-1) == 2
+    assert _q(L, h=8) == 3                                  # hadamard size
+    assert _q(L, axis=2) == 3
+    assert _q(L, rnd=5) == 3
+    assert _q(L, dtype=3) == 3
+    assert _q(L, ldx=32) == 3                               # ldx < cols
+    assert _q(L, ldq=16) == 3                               # ldq < L/2
+    assert _q(L, x=None) == 1
+    assert _q(L, q=None) == 1
+    assert _q(L, x=(1 << 12) + 2) == 4                      # x not 16-byte aligned
+    assert _q(L, ldx=68) == 4                               # row stride not a multiple of 16 bytes
+    assert _q(L, ldq=40) == 4
+    assert _q(L, rows=0) == 0 and _q(L, rows=0, x=None) == 0  # empty: nothing to do
+
+
+def test_gemm_argument_errors(L):
+    def g(aq=1 << 12, lda=32, bq=1 << 12, ldb=32, M=8, N=8, K=64, c=1 << 12, ldc=8):
+        return L.mxfp4_gemm(aq, lda, 1 << 12, 2, bq, ldb, 1 << 12, 2, M, N, K, 1.0, c, ldc, None)
+    assert g(K=48) == 2
+    assert g(M=-2) == 2
+    assert g(lda=16) == 3
+    assert g(ldc=4) == 3
+    assert g(c=None) == 1
+    assert g(aq=None) == 1
+    assert g(aq=(1 << 12) + 8) == 4
+    assert g(M=0) == 0 and g(N=0, c=None) == 0
+
+
+def test_linear_argument_errors(L):
+    import mxfp4_block_scaled_h16_amd as mx
+    cfg = mx.LinearCfg(16, 0, 0, 0)
+    bad = mx.LinearCfg(12, 0, 0, 0)
+    f = L.mxfp4_linear_fprop
+    ws = mx.workspace_bytes(mx.FPROP, 64, 64, 64)
+    assert f(1 << 12, 1 << 12, 64, 64, 64, None, 1 << 12, ws, 1 << 12, None) == 1
+    assert f(1 << 12, 1 << 12, 64, 64, 64, ctypes.byref(bad), 1 << 12, ws, 1 << 12, None) == 3
+    assert f(1 << 12, 1 << 12, 64, 48, 64, ctypes.byref(cfg), 1 << 12, ws, 1 << 12, None) == 2
+    assert f(1 << 12, 1 << 12, 64, 64, 64, ctypes.byref(cfg), 1 << 12, ws - 1, 1 << 12, None) == 5
+    assert f(1 << 12, 1 << 12, 64, 64, 64, ctypes.byref(cfg), None, ws, 1 << 12, None) == 5
+    assert f(1 << 12, 1 << 12, 64, 64, 64, ctypes.byref(cfg), (1 << 12) + 16, ws, 1 << 12, None) == 4
+    assert f(None, 1 << 12, 64, 64, 64, ctypes.byref(cfg), 1 << 12, ws, 1 << 12, None) == 1
+    # Dgrad contracts over N, Wgrad over M
+    assert L.mxfp4_linear_dgrad(1 << 12, 1 << 12, 64, 64, 40, ctypes.byref(cfg), 1 << 12, 1 << 30,
+                                1 << 12, None) == 2
+    assert L.mxfp4_linear_wgrad(1 << 12, 1 << 12, 40, 64, 64, ctypes.byref(cfg), 1 << 12, 1 << 30,
+                                1 << 12, None) == 2
+    assert f(1 << 12, 1 << 12, 0, 64, 64, ctypes.byref(cfg), None, 0, None, None) == 0
