@@ -32,7 +32,11 @@ def random_operand(rng, outer, K, scale_lo=110, scale_hi=140):
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 64), (128, 128, 128), (256, 256, 512), (200, 72, 96),
-                                   (1, 1, 32), (33, 129, 160), (384, 130, 1024), (64, 64, 4096)])
+                                   (1, 1, 32), (33, 129, 160), (384, 130, 1024), (64, 64, 4096),
+                                   # 256-multiple K: the tiled kernel, with ragged M / N tails and
+                                   # tile counts that are and are not multiples of 8
+                                   (1000, 520, 512), (2048, 1536, 1024), (300, 700, 256),
+                                   (513, 257, 768), (4096, 512, 2048)])
 def test_gemm_random_codes(M, N, K):
     import mxfp4_block_scaled_h16_amd as mx
     rng = np.random.default_rng(M * 7 + N * 13 + K)
