@@ -10,6 +10,7 @@
 // 32 x 32 FP32 result sits in 16 registers per lane: register i of lane l is row
 // 8 (i / 4) + 4 (l / 32) + (i % 4), column l % 32.
 #include <climits>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -18,6 +19,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kFmtFp4 = 4;  // format selector of the f8f6f4 MFMA family for E2M1
 
@@ -99,48 +101,78 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
 }
 
 // ------------------------------------------------------------------------------------------
-// Tiled kernel: 256 x 256 workgroup tile, four wavefronts of 128 x 128 (4 x 4 MFMA tiles, 256
-// accumulator registers each, one wavefront per SIMD). Operand codes move HBM -> LDS by direct
-// 16-byte-per-lane DMA (global_load_lds_dwordx4), double-buffered over K stages of 256 values
-// (128 bytes per row). Rows are stored with their 16-byte chunks XOR-swizzled so that the
-// fragment reads (ds_read_b128, one MX block per lane) hit distinct banks. Scale bytes go straight
-// from memory into registers (8 per row and stage), shifted per lane so the MFMA's byte selector
-// is the same for the whole wavefront.
-// Requirements (checked by the dispatcher): K % 256 == 0, scales rows 8-byte aligned.
+// Pipelined kernel: 256 x 256 workgroup tile, four wavefronts of 128 x 128 (4 x 4 MFMA tiles,
+// 256 accumulator registers each, one wavefront per SIMD).
+//
+// The MFMA pipe of a SIMD only stays busy if its single wavefront never stops issuing, so the
+// K loop is software-pipelined around it:
+//  * operand codes move HBM -> LDS by direct 16-byte-per-lane DMA into a ring of four stage
+//    buffers of 128 K values (64 bytes per row), issued three stages ahead; each wait is for the
+//    oldest stage only (vmcnt with the exact number of younger loads);
+//  * scale bytes move the same way, 16 per row (four stages) at a time, into two LDS slots;
+//  * LDS fragment and scale reads for the next 64-wide sub-step are issued between the MFMAs of
+//    the current one, and so are the DMA instructions;
+//  * the product is formed transposed (B as the MFMA's first operand), so each lane ends with
+//    four consecutive output columns per register quad and stores 16 bytes at a time.
+// Rows of a stage buffer hold their four 16-byte chunks XOR-permuted by bits 2-3 of the row: the
+// LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, 64 banks) at a time, and the 16 rows
+// those lanes read then land in 16 distinct bank groups.
+// Requirements (checked by the dispatcher): K % 512 == 0; scale rows 16-byte aligned; row byte
+// offsets fit in 32 bits.
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kRowBytes = 128;                  // codes per row per stage (256 E2M1 values)
-constexpr int kStageK = 2 * kRowBytes;          // K values per stage
-constexpr int kABytes = kBM * kRowBytes;        // 32 KB
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;  // 64 KB
-constexpr int kRowsPerDma = 1024 / kRowBytes;   // one wave-wide 16 B/lane DMA covers 8 rows
-constexpr int kDmaPerWave = kBM / kRowsPerDma / 4;  // 8 per operand per wavefront
+constexpr int kStageK = 128;                          // K values per stage
+constexpr int kRowBytes = kStageK / 2;                // 64 bytes of codes per row per stage
+constexpr int kABytes = kBM * kRowBytes;              // 16 KB
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;  // 32 KB
+constexpr int kNumBuf = 4;                            // stage ring; a group = 4 stages
+constexpr int kScaleSlot = (kBM + kBN) * 16;          // 8 KB: 16 scale bytes per row per group
+constexpr int kScaleBase = kNumBuf * kStageBytes;     // two scale slots after the stage ring
+constexpr int kLdsBytes = kScaleBase + 2 * kScaleSlot;  // 144 KB
+constexpr int kRowsPerDma = 1024 / kRowBytes;         // one wave-wide 16 B/lane DMA covers 16 rows
+constexpr int kDmaPerOperand = kBM / kRowsPerDma / 4; // 4 per operand per wavefront
+constexpr int kDmaPerStage = 2 * kDmaPerOperand;      // 8 VMEM instructions per wavefront
+constexpr int kDmaPerScales = 2;                      // 1 per operand per wavefront per group
 
-// chunk permutation of a row: rows r..r+7 and every other row of r..r+15 all land in distinct
-// 16-byte bank groups when the same logical chunk is read
-__device__ __forceinline__ int chunk_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int chunk_perm(int row) { return (row >> 2) & 3; }
 
-__device__ __forceinline__ void mfma_tile(v16f &acc, const u32x4 &a, const u32x4 &b, int sa, int sb,
-                                          int opsel_hi)
+template <int OPSEL>
+__device__ __forceinline__ void mfma_t(v16f &acc, const u32x4 &b, const u32x4 &a, uint32_t sb, uint32_t sa)
 {
-    const v8i va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
     const v8i vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-    if (opsel_hi)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, kFmtFp4, kFmtFp4, 2, sa, 2, sb);
-    else
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, kFmtFp4, kFmtFp4, 0, sa, 0, sb);
+    const v8i va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc, kFmtFp4, kFmtFp4, OPSEL, (int)sb,
+                                                          OPSEL, (int)sa);
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_mxfp4_tiled(
+// s_waitcnt vmcnt(N) with N < 64 (gfx9 encoding: low 4 bits in [3:0], high 2 bits in [15:14];
+// expcnt and lgkmcnt fields left at their "no wait" maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct PipeCtx {
+    const uint8_t *aq, *bq, *as, *bs;
+    uint32_t a_off[kDmaPerOperand], b_off[kDmaPerOperand];  // per-lane code offsets
+    uint32_t as_off, bs_off;                                 // per-lane scale offsets
+    int dma_row0;                                            // first stage row of this wave's DMA
+    int a_frag, b_frag, chunk0, chunk1;                      // fragment read offsets
+    int sa_lds, sb_lds;                                      // scale word offsets (stage 0)
+};
+
+__global__ __launch_bounds__(256, 1) void gemm_mxfp4_pipelined(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
     int M, int N, int K, float alpha, float *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
     // tile order: consecutive workgroups are spread over the 8 XCDs; give each XCD a contiguous
     // range of tiles, walked column-panel by column-panel in groups of 8 row panels
@@ -155,48 +187,72 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_tiled(
     const int m0 = tm * kBM, n0 = tn * kBN;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int r = lane & 31, half = lane >> 5;
-    const int swz = chunk_swizzle(r);
 
-    // DMA sources: instruction (wave, t) fills LDS rows [8 (8 wave + t), + 8); lane L writes the
-    // 16 bytes at row 8 (8 wave + t) + L / 8, physical chunk L % 8 = logical chunk ^ swizzle
-    uint32_t a_off[kDmaPerWave], b_off[kDmaPerWave];
+    PipeCtx p;
+    p.aq = aq;
+    p.bq = bq;
+    p.as = as;
+    p.bs = bs;
+    // code DMA: instruction u of this wavefront fills stage rows [16 (4 wave + u), + 16) of each
+    // operand; lane L writes the 16 bytes at row + L / 4, physical chunk L % 4
+    p.dma_row0 = kRowsPerDma * kDmaPerOperand * wave;
 #pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) {
-        const int row = kRowsPerDma * (kDmaPerWave * wave + u) + lane / 8;
-        const int chunk = (lane % 8) ^ chunk_swizzle(row);
-        a_off[u] = (uint32_t)(min(m0 + row, M - 1) * lda + 16 * chunk);
-        b_off[u] = (uint32_t)(min(n0 + row, N - 1) * ldb + 16 * chunk);
+    for (int u = 0; u < kDmaPerOperand; ++u) {
+        const int row = p.dma_row0 + kRowsPerDma * u + lane / 4;
+        const int chunk = (lane % 4) ^ chunk_perm(row);
+        p.a_off[u] = (uint32_t)(min(m0 + row, M - 1) * lda + 16 * chunk);
+        p.b_off[u] = (uint32_t)(min(n0 + row, N - 1) * ldb + 16 * chunk);
     }
-    // scale sources of this lane's fragment rows
-    const uint8_t *sa_ptr[4], *sb_ptr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sa_ptr[i] = as + (int64_t)min(m0 + wm * 128 + 32 * i + r, M - 1) * ldas;
-        sb_ptr[i] = bs + (int64_t)min(n0 + wn * 128 + 32 * i + r, N - 1) * ldbs;
-    }
+    // scale DMA: wavefront w brings rows [64 w, 64 w + 64) of each operand, 16 bytes per lane
+    p.as_off = (uint32_t)(min(m0 + 64 * wave + lane, M - 1) * ldas);
+    p.bs_off = (uint32_t)(min(n0 + 64 * wave + lane, N - 1) * ldbs);
+    // fragment and scale reads of this lane
+    const int perm = chunk_perm(r);
+    p.a_frag = (wm * 128 + r) * kRowBytes;
+    p.b_frag = kABytes + (wn * 128 + r) * kRowBytes;
+    p.chunk0 = 16 * ((0 + half) ^ perm);
+    p.chunk1 = 16 * ((2 + half) ^ perm);
+    p.sa_lds = kScaleBase + 16 * (wm * 128 + r);
+    p.sb_lds = kScaleBase + 16 * (kBM + wn * 128 + r);
 
-    auto dma_stage = [&](int buf, int kstage) {
-        uint8_t *dst = lds + buf * kStageBytes;
-        const int kb = kstage * kRowBytes;
+    auto dma = [&](int buf, int stage) {
+        uint8_t *dst = lds + buf * kStageBytes + p.dma_row0 * kRowBytes;
+        const uint8_t *asrc = p.aq + (uint32_t)stage * kRowBytes;
+        const uint8_t *bsrc = p.bq + (uint32_t)stage * kRowBytes;
 #pragma unroll
-        for (int u = 0; u < kDmaPerWave; ++u) {
-            const int row0 = kRowsPerDma * (kDmaPerWave * wave + u);
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(aq + a_off[u] + kb),
-                                             (lds_void_t *)(dst + row0 * kRowBytes), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(bq + b_off[u] + kb),
-                                             (lds_void_t *)(dst + kABytes + row0 * kRowBytes), 16, 0, 0);
-        }
+        for (int u = 0; u < kDmaPerOperand; ++u)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(asrc + p.a_off[u]),
+                                             (lds_void_t *)(dst + u * 1024), 16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kDmaPerOperand; ++u)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(bsrc + p.b_off[u]),
+                                             (lds_void_t *)(dst + kABytes + u * 1024), 16, 0, 0);
     };
-    // 8 scale bytes per fragment row and stage, kept raw until the stage is computed (shifting
-    // them at load time would make the wavefront wait for the loads just issued)
-    auto load_scales = [&](int kstage, uint64_t (&sa)[4], uint64_t (&sb)[4]) {
+    auto dma_scales = [&](int g) {
+        uint8_t *dst = lds + kScaleBase + (g & 1) * kScaleSlot + 1024 * wave;
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(p.as + 16 * g + p.as_off), (lds_void_t *)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(p.bs + 16 * g + p.bs_off),
+                                         (lds_void_t *)(dst + kBM * 16), 16, 0, 0);
+    };
+    auto read_frags = [&](int buf, int chunk, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+        const uint8_t *src = lds + buf * kStageBytes;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sa[i] = *reinterpret_cast<const uint64_t *>(sa_ptr[i] + 8 * kstage);
-            sb[i] = *reinterpret_cast<const uint64_t *>(sb_ptr[i] + 8 * kstage);
+            fa[i] = *reinterpret_cast<const u32x4 *>(src + p.a_frag + 32 * i * kRowBytes + chunk);
+            fb[i] = *reinterpret_cast<const u32x4 *>(src + p.b_frag + 32 * i * kRowBytes + chunk);
+        }
+    };
+    // this lane's scale words of stage s (byte 2 kk + half of word s % 4 of its rows)
+    auto read_scales = [&](int s, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+        const int off = ((s >> 2) & 1) * kScaleSlot + 4 * (s & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa[i] = *reinterpret_cast<const uint32_t *>(lds + p.sa_lds + off + 16 * 32 * i);
+            sb[i] = *reinterpret_cast<const uint32_t *>(lds + p.sb_lds + off + 16 * 32 * i);
         }
     };
 
@@ -208,73 +264,143 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_tiled(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int nk = K / kStageK;
-    uint64_t sa_raw[4], sb_raw[4], sa_nxt[4], sb_nxt[4];
-    dma_stage(0, 0);
-    load_scales(0, sa_raw, sb_raw);
+    // 16 MFMAs of one 64-wide sub-step; transposed product: acc[i][j] holds C^T tile (j, i)
+    auto mfma_step = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4], const uint32_t (&sa)[4],
+                         const uint32_t (&sb)[4], auto opsel) {
+        uint32_t xa[4], xb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xa[i] = sa[i] >> (8 * half);
+            xb[i] = sb[i] >> (8 * half);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                mfma_t<decltype(opsel)::value>(acc[i][j], fb[j], fa[i], xb[j], xa[i]);
+    };
 
-    const int a_row0 = wm * 128 + r;
-    const int b_row0 = wn * 128 + r;
-    for (int ks = 0; ks < nk; ++ks) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this stage's DMA and scales landed
-        __syncthreads();                      // ... for every wavefront; the other buffer is free
-        // byte 0 / byte 2 of each word = this lane's block for even / odd K64 sub-steps
-        uint32_t sa[4][2], sb[4][2];
+    const int nk = K / kStageK;  // multiple of 4, >= 4
+    const int ngroups = nk / 4;
+    u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+    uint32_t sa0[4], sb0[4], sa1[4], sb1[4];
+
+    // prologue: scales of stages 0-3, then stages 0, 1, 2; wait for the scales and stage 0
+    dma_scales(0);
+    dma(0, 0);
+    dma(1, 1);
+    dma(2, 2);
+    wait_vmcnt<2 * kDmaPerStage>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, p.chunk0, fa0, fb0);
+    read_scales(0, sa0, sb0);
+
+    // One stage s = 4 g + J (ring buffer J). WAITN = the number of loads issued after those of
+    // stage s + 1 at the point of the wait (-1: no next stage); DMA_NEXT: issue stage s + 3;
+    // SCALES_NEXT: issue the scales of group g + 1.
+    auto stage = [&](int g, auto J, auto WAITN, auto DMA_NEXT, auto SCALES_NEXT) {
+        constexpr int j = decltype(J)::value;
+        constexpr int waitn = decltype(WAITN)::value;
+        const int s = 4 * g + j;
+        // sub-step 0: read sub-step 1's fragments while these MFMAs run, two after each of the
+        // first four MFMAs
+        read_frags(j, p.chunk1, fa1, fb1);
+        mfma_step(fa0, fb0, sa0, sb0, std::integral_constant<int, 0>());
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (waitn >= 0) {
+            // stage s + 1 has landed for every wavefront, and every wavefront is done reading
+            // stage s - 1's buffer, which the DMA of stage s + 3 overwrites
+            wait_vmcnt<waitn>();
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(DMA_NEXT)::value) dma((j + 3) % 4, s + 3);
+        if constexpr (decltype(SCALES_NEXT)::value) dma_scales(g + 1);
+        if constexpr (waitn >= 0) {
+            read_frags((j + 1) % 4, p.chunk0, fa0, fb0);
+            read_scales(s + 1, sa1, sb1);
+        }
+        mfma_step(fa1, fb1, sa0, sb0, std::integral_constant<int, 2>());
+        // the DMA first (it has the longest way to go), one or two instructions per MFMA, then
+        // the next stage's fragment and scale reads, early enough to land before sub-step 0
+        constexpr int nvmem = (decltype(DMA_NEXT)::value ? kDmaPerStage : 0) +
+                              (decltype(SCALES_NEXT)::value ? kDmaPerScales : 0);
+        constexpr int nds = waitn >= 0 ? 12 : 0;
+        constexpr int nlead = (nvmem + 1) / 2 + (nds + 1) / 2;
+#pragma unroll
+        for (int k = 0; k < (nvmem + 1) / 2; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read (DMA)
+        }
+#pragma unroll
+        for (int k = 0; k < (nds + 1) / 2; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16 - nlead, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sa[i][0] = (uint32_t)sa_raw[i] >> (8 * half);
-            sa[i][1] = (uint32_t)(sa_raw[i] >> 32) >> (8 * half);
-            sb[i][0] = (uint32_t)sb_raw[i] >> (8 * half);
-            sb[i][1] = (uint32_t)(sb_raw[i] >> 32) >> (8 * half);
+            sa0[i] = sa1[i];
+            sb0[i] = sb1[i];
         }
-        if (ks + 1 < nk) {
-            dma_stage((ks + 1) & 1, ks + 1);
-            load_scales(ks + 1, sa_nxt, sb_nxt);
-        }
-        const uint8_t *sbuf = lds + (ks & 1) * kStageBytes;
-        // fragments of sub-step kk + 1 are read while the 16 MFMAs of sub-step kk run
-        u32x4 fa[2][4], fb[2][4];
-        auto read_frags = [&](int kk, u32x4 (&a)[4], u32x4 (&b)[4]) {
-            const int chunk = (2 * kk + half) ^ swz;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = *reinterpret_cast<const u32x4 *>(sbuf + (a_row0 + 32 * i) * kRowBytes + 16 * chunk);
-                b[i] = *reinterpret_cast<const u32x4 *>(sbuf + kABytes + (b_row0 + 32 * i) * kRowBytes + 16 * chunk);
-            }
-        };
-        read_frags(0, fa[0], fb[0]);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int cur = kk & 1;
-            if (kk < 3) read_frags(kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-            __builtin_amdgcn_sched_barrier(0);  // the reads above are issued before these MFMAs
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    mfma_tile(acc[i][j], fa[cur][i], fb[cur][j], (int)sa[i][kk >> 1], (int)sb[j][kk >> 1],
-                              kk & 1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa_raw[i] = sa_nxt[i];
-            sb_raw[i] = sb_nxt[i];
-        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using W8 = std::integral_constant<int, kDmaPerStage>;
+    using W10 = std::integral_constant<int, kDmaPerStage + kDmaPerScales>;
+    using W0 = std::integral_constant<int, 0>;
+    using WNone = std::integral_constant<int, -1>;
+    using T = std::true_type;
+    using F = std::false_type;
+
+    for (int g = 0; g + 1 < ngroups; ++g) {
+        stage(g, I0(), W8(), T(), T());
+        stage(g, I1(), W10(), T(), F());
+        stage(g, I2(), W10(), T(), F());
+        stage(g, I3(), W8(), T(), F());
+    }
+    {
+        const int g = ngroups - 1;
+        stage(g, I0(), W8(), T(), F());
+        stage(g, I1(), W8(), F(), F());
+        stage(g, I2(), W0(), F(), F());
+        stage(g, I3(), WNone(), F(), F());
     }
 
+    // epilogue: acc[i][j] register q * 4 + t of lane (r, half) is
+    // C[m0 + 128 wm + 32 i + r][n0 + 128 wn + 32 j + 8 q + 4 half + t]
+    const bool full_cols = n0 + kBN <= N && (ldc % 4) == 0 && ((uintptr_t)c % 16) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 128 + 32 * i + r;
+        if (m >= M) continue;
+        float *crow = c + (int64_t)m * ldc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wn * 128 + 32 * j + r;
-            if (n >= N) continue;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + wm * 128 + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
-                if (m < M) c[(int64_t)m * ldc + n] = alpha * acc[i][j][e];
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * half;
+                const f32x4v v = {alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1],
+                                  alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]};
+                if (full_cols) {
+                    *reinterpret_cast<f32x4v *>(crow + n) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) crow[n + e] = v[e];
+                }
             }
-        }
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ c, int64_t M, int64_t N,
@@ -298,14 +424,14 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
                        const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs, int64_t M,
                        int64_t N, int64_t K, float alpha, float *c, int64_t ldc, hipStream_t stream)
 {
-    const bool scales_aligned = ((uintptr_t)as % 8 == 0) && ((uintptr_t)bs % 8 == 0) && ldas % 8 == 0 &&
-                                ldbs % 8 == 0;
+    const bool scales_aligned = ((uintptr_t)as % 16 == 0) && ((uintptr_t)bs % 16 == 0) &&
+                                ldas % 16 == 0 && ldbs % 16 == 0;
     const bool offsets_fit = (int64_t)(M - 1) * lda + lda <= INT32_MAX && (int64_t)(N - 1) * ldb + ldb <= INT32_MAX;
-    if (K % kStageK == 0 && K > 0 && scales_aligned && offsets_fit) {
+    if (K % 512 == 0 && K > 0 && scales_aligned && offsets_fit) {
         const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
-        return launch(gemm_mxfp4_tiled, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream, aq,
-                      lda, as, ldas, bq, ldb, bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m,
-                      tiles_n);
+        return launch(gemm_mxfp4_pipelined, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream,
+                      aq, lda, as, ldas, bq, ldb, bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc,
+                      tiles_m, tiles_n);
     }
     const dim3 grid((unsigned)((N + kTileN - 1) / kTileN), (unsigned)((M + kTileM - 1) / kTileM));
     return launch(gemm_mxfp4_simple, grid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
