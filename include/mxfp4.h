@@ -83,7 +83,8 @@ typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
  *            (the Wgrad token axis and the Dgrad weight operand).
  *   hadamard 0 (no rotation), 16 or 32; rounding MXFP4_RNE or MXFP4_SR_PHILOX with (seed, stream).
  *
- * Requirements: rows, cols >= 0; L % 32 == 0; ldx >= cols; ldq >= L/2; lds >= L/32.
+ * Requirements: rows, cols >= 0; L % 32 == 0; at most 2^30 32-element blocks (rows * cols / 32);
+ * ldx >= cols; ldq >= L/2; lds >= L/32.
  * Alignment: x 16-byte aligned and ldx * sizeof(element) a multiple of 16; q 16-byte aligned and
  * ldq % 16 == 0. Empty tensors return MXFP4_OK without a launch.
  */

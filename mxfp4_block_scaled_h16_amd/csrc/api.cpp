@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int64_t kMaxBlocks = (int64_t)1 << 31;  // 32-element blocks per quantize launch
+constexpr int64_t kMaxBlocks = (int64_t)1 << 30;  // 32-element blocks per quantize launch
 constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }

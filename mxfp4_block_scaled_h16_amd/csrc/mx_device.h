@@ -66,34 +66,43 @@ __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits)
     return e > 2u ? e - 2u : 0u;
 }
 
-// 2^(127 - S) as binary32 for S <= 252 (exponent field 254 - S lies in [2, 254]).
+// ---------------------------------------------------------------------------- E2M1 encode -----
+// Nearest-even encoding uses gfx950's v_cvt_scalef32_pk_fp4_f32, which converts two binary32
+// values divided by a binary32 scale to two E2M1 codes (first value in the low nibble) with
+// ties to the even code, saturation at 6 and the sign bit of the scaled value kept for zero
+// results -- the encoding defined above. Dividing by 2^(S - 127) is exact for S in [1, 252]
+// (every finite block has S <= 252); an S = 0 block is pre-multiplied by 2 and divided by
+// 2^-126 so the scale operand never is a subnormal.
+
+// binary32 divisor 2^(S - 127) for S in [1, 252] (exponent field S, zero mantissa)
+__device__ __forceinline__ float e8m0_divisor(uint32_t s) { return __uint_as_float((s > 1u ? s : 1u) << 23); }
+
+// Codes of 8 consecutive values (scaled by 2^(127 - S)) as one word, element k in nibble k.
+__device__ __forceinline__ uint32_t encode8_nearest(const float *v, float divisor)
+{
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], divisor, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], divisor, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], divisor, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], divisor, 3);
+    return w;
+}
+
+// The S = 0 case of the divisor rule above: double every value of the block (exact).
+template <int N>
+__device__ __forceinline__ void prescale_if_zero_scale(float *v, uint32_t s)
+{
+    if (s == 0u) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] *= 2.0f;
+    }
+}
+
+// 2^(127 - S) as binary32 multiplier for S in [0, 252] (exponent field 254 - S in [2, 254]).
 __device__ __forceinline__ float e8m0_reciprocal(uint32_t s)
 {
     const uint32_t sc = s < 252u ? s : 252u;
     return __uint_as_float((254u - sc) << 23);
-}
-
-// ---------------------------------------------------------------------------- E2M1 encode -----
-// Nearest-even E2M1 magnitude index of a >= 0 (a < 8 after scaling). Adding 1.5 * 2^23 * q
-// rounds a to a multiple of the grid step q in IEEE nearest-even, and the integer difference of
-// the sums' bit patterns counts those multiples; the low bit of that count is the code's mantissa
-// bit, so IEEE ties-to-even is the E2M1 ties-to-even. Saturates at index 7 (value 6).
-__device__ __forceinline__ uint32_t e2m1_nearest(float a)
-{
-    float bias;
-    uint32_t first;
-    if (a < 2.0f) {            // step 0.5: indices 0..4
-        bias = 6291456.0f;     // 1.5 * 2^22
-        first = 0u;
-    } else if (a < 4.0f) {    // step 1: values 2, 3, 4 -> indices 4, 5, 6
-        bias = 12582912.0f;    // 1.5 * 2^23
-        first = 2u;
-    } else {                   // step 2: values 4, 6, 8 -> indices 6, 7, (8 -> 7)
-        bias = 25165824.0f;    // 1.5 * 2^24
-        first = 4u;
-    }
-    const uint32_t k = __float_as_uint(a + bias) - __float_as_uint(bias) + first;
-    return k < 7u ? k : 7u;
 }
 
 // Stochastic E2M1 magnitude index of a >= 0 with random word r: saturate at 6, else round up to
@@ -156,45 +165,50 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return r;
 }
 
-// ---------------------------------------------------------------------------- one block -------
-// Encode 32 rotated values into four words of codes (8 codes per word, even element low) and
-// return the scale byte. index0 = position of v[0] in the quantized output (o * L + j); it is a
-// multiple of 32, so the block uses exactly 8 Philox counters.
-template <bool SR>
-__device__ __forceinline__ uint32_t encode_block(const float *v, uint32_t *words, uint64_t index0,
-                                                 uint32_t key0, uint32_t key1, uint32_t stream_id)
+// ---------------------------------------------------------------------------- stochastic -----
+// Stochastic codes of 8 consecutive values y[0..7] (not yet scaled) whose first element has
+// position index0 (a multiple of 8) in the quantized output: two Philox blocks, word k of
+// block (index0 / 4 + b) for element 4 b + k.
+__device__ __forceinline__ uint32_t encode8_stochastic(const float *y, uint32_t s, uint64_t index0,
+                                                       uint32_t key0, uint32_t key1, uint32_t stream_id)
 {
-    uint32_t amax = 0u;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[i]));
-    const uint32_t s = e8m0_from_amax_bits(amax);
     const float mul = e8m0_reciprocal(s);
+    const uint64_t c = index0 >> 2;
+    const Philox4 r0 = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), stream_id, 0u, key0, key1);
+    const uint64_t c1 = c + 1;
+    const Philox4 r1 = philox4x32_10((uint32_t)c1, (uint32_t)(c1 >> 32), stream_id, 0u, key0, key1);
+    uint32_t word = 0u;
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-        uint32_t word = 0u;
-        if constexpr (SR) {
-            const uint64_t ctr = (index0 >> 2) + (uint64_t)(2 * wd);
-            const Philox4 r0 = philox4x32_10((uint32_t)ctr, (uint32_t)(ctr >> 32), stream_id, 0u, key0, key1);
-            const uint64_t ctr1 = ctr + 1;
-            const Philox4 r1 = philox4x32_10((uint32_t)ctr1, (uint32_t)(ctr1 >> 32), stream_id, 0u, key0, key1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float y = v[8 * wd + e];
-                const uint32_t rnd = e < 4 ? r0.w[e] : r1.w[e - 4];
-                const uint32_t code = e2m1_stochastic(fabsf(y * mul), rnd) | sign_nibble(y);
-                word |= code << (4 * e);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float y = v[8 * wd + e];
-                const uint32_t code = e2m1_nearest(fabsf(y * mul)) | sign_nibble(y);
-                word |= code << (4 * e);
-            }
-        }
-        words[wd] = (s == 0xFFu) ? 0u : word;
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t rnd = e < 4 ? r0.w[e] : r1.w[e - 4];
+        word |= (e2m1_stochastic(fabsf(y[e] * mul), rnd) | sign_nibble(y[e])) << (4 * e);
     }
-    return s;
+    return word;
+}
+
+// ---------------------------------------------------------------------------- cross-lane ------
+// Value of lane (l ^ X) for X in {1, 2} (DPP quad permutation; every lane must be active).
+template <int X>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t v)
+{
+    static_assert(X == 1 || X == 2, "quad xor");
+    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, true);
+}
+
+// One Walsh-Hadamard stage whose pairs straddle lanes l and l ^ X (each lane holds 8 values,
+// the lane with bit X set holds the higher-index element of every pair): the lower lane keeps
+// u + w, the upper lane u - w, computed as u + (-w) (IEEE subtraction), so the results are
+// bit-identical to the in-register stage.
+template <int X>
+__device__ __forceinline__ void fwht_cross_stage(float *v, bool upper)
+{
+    const uint32_t flip = upper ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float other = __uint_as_float(quad_xor<X>(__float_as_uint(v[i])));
+        v[i] = other + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+    }
 }
 
 }  // namespace mx
