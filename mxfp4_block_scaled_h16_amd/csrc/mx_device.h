@@ -105,29 +105,23 @@ __device__ __forceinline__ float e8m0_reciprocal(uint32_t s)
     return __uint_as_float((254u - sc) << 23);
 }
 
-// Stochastic E2M1 magnitude index of a >= 0 with random word r: saturate at 6, else round up to
-// the next grid value iff r < 2^32 * (fractional position of a between its two grid neighbours).
-// For integer r, r < t is r < ceil(t); every product below is exact in binary32.
+// Stochastic E2M1 magnitude index of a = |v| >= 0 with random word r: saturate at 6, else round
+// up to the next grid value iff r < 2^32 f, f = fractional position of a between its two grid
+// neighbours. Read from the bit pattern A of a:
+//  * a in [1, 6): the step is half the value's leading power of two, so the magnitude index of
+//    the lower neighbour is 2 * (biased exponent) + (top mantissa bit) - 252 and 2^32 f is the
+//    remaining 22 mantissa bits, A << 10;
+//  * a in [1/2, 1): lower neighbour 1/2 (index 1), step 1/2, 2^32 f = the 23 mantissa bits, A << 9;
+//  * a < 1/2: lower neighbour 0, f = 2 a, and r < 2^33 a is r < ceil(2^33 a) (exact products).
 __device__ __forceinline__ uint32_t e2m1_stochastic(float a, uint32_t r)
 {
-    if (!(a < 6.0f)) return 7u;
-    float inv_step;
-    uint32_t first;
-    if (a < 2.0f) {
-        inv_step = 2.0f;
-        first = 0u;
-    } else if (a < 4.0f) {
-        inv_step = 1.0f;
-        first = 2u;
-    } else {
-        inv_step = 0.5f;
-        first = 4u;
-    }
-    const float t = a * inv_step;
-    const float lo = floorf(t);
-    const float frac = t - lo;
-    const uint32_t threshold = (uint32_t)ceilf(frac * 4294967296.0f);
-    return (uint32_t)lo + first + (r < threshold ? 1u : 0u);
+    const uint32_t A = __float_as_uint(a);
+    const bool ge1 = A >= 0x3F800000u, ge_half = A >= 0x3F000000u;
+    const uint32_t t_small = (uint32_t)ceilf(a * 8589934592.0f);
+    const uint32_t lo = ge1 ? (A >> 22) - 252u : (ge_half ? 1u : 0u);
+    const uint32_t t = ge1 ? (A << 10) : (ge_half ? (A << 9) : t_small);
+    const uint32_t mag = lo + (r < t ? 1u : 0u);
+    return A >= 0x40C00000u ? 7u : mag;  // a >= 6 (or NaN, whose block is discarded)
 }
 
 // Sign of a binary32 value as the E2M1 sign bit (bit 3).
