@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the MXFP4 + block-Hadamard linear-layer GEMMs on one MI355X.
 
-One step = the whole hot path over one batch of synthetic input: for one linear layer,
-  Fprop  Y  = X W^T      (X and W rotated by H16 and quantized along K, nearest-even)
+One step = the whole hot path over one batch of synthetic input. For each linear projection of
+the workload it runs the passes the workload names:
+  Fprop  Y  = X W^T      (X and W rotated and quantized along K, nearest-even)
   Dgrad  dX = dY W       (dY along N, W along N -- transposed quantize -- nearest-even)
-  Wgrad  dW = dY^T X     (dY and X along the token axis M -- transposed -- stochastic rounding)
-each as two quantize launches and one block-scaled FP4 GEMM through the C ABI
-(mxfp4_quantize, mxfp4_gemm). This follows the gist.science summary of "MXFP4 LLM pretraining",
-section 방법론 (Methodology): all three GEMMs in MXFP4 with the deterministic H16 rotation; the
-stochastic rounding on the weight-gradient operands is the full-layer recipe of this benchmark.
+  Wgrad  dW = dY^T X     (dY and X along the token axis M -- transposed -- Philox stochastic
+                          rounding on both operands)
+Every pass is quantize launches plus one block-scaled FP4 GEMM through the C ABI
+(mxfp4_quantize, mxfp4_gemm); an activation read by several projections is quantized once per
+axis. This follows the gist.science summary "기술 요약: MXFP4 를 활용한 대규모 언어 모델 사전
+학습", section 방법론 (Methodology): all three GEMMs in MXFP4 behind the deterministic H16
+rotation; stochastic rounding on the weight-gradient operands is the full-layer recipe here.
 
-Default workload: the Llama-3.1-8B QKV projection, M = 8192 tokens, K = 4096, N = 6144.
-Prints ONE JSON line (rank 0). Inputs are resident in HBM before the timed region starts.
+Default workload: the Llama-3.1-8B QKV projection, M = 8192 tokens, K = 4096, N = 6144,
+Fprop + Dgrad + Wgrad. `--workload layer` runs all 7 projections of one decoder layer.
+Prints ONE JSON line. Inputs are resident in HBM before the timed region starts.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,12 +31,17 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4/FP6 matrix peak, published
 QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0   # bf16 in, 4-bit code out, one E8M0 byte per 32
 
+# name: (description, [(projection, K, N)], input of each projection, passes, tokens)
+LLAMA_PROJ = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
+              ("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)]
+LLAMA_INPUT = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "o_in", "gate": "mlp_in",
+               "up": "mlp_in", "down": "down_in"}
 WORKLOADS = {
-    # name: (M tokens, K in_features, N out_features, description)
-    "qkv": (8192, 4096, 6144, "Llama-3.1-8B QKV projection"),
-    "small": (256, 512, 256, "single small layer"),
-    "gateup": (8192, 4096, 28672, "Llama-3.1-8B fused gate+up projection"),
-    "down": (8192, 14336, 4096, "Llama-3.1-8B down projection"),
+    "qkv": ("Llama-3.1-8B QKV projection Fprop+Dgrad+Wgrad", [("qkv", 4096, 6144)], "FDW", 8192),
+    "small": ("single small layer Fprop+Dgrad+Wgrad", [("small", 512, 256)], "FDW", 256),
+    "gateup": ("Llama-3.1-8B fused gate+up projection Fprop+Dgrad", [("gateup", 4096, 28672)], "FD", 8192),
+    "down": ("Llama-3.1-8B down projection Wgrad", [("down", 14336, 4096)], "W", 8192),
+    "layer": ("Llama-3.1-8B decoder layer, 7 projections x Fprop+Dgrad+Wgrad", LLAMA_PROJ, "FDW", 8192),
 }
 
 
@@ -50,120 +58,164 @@ def parse_args():
     return p.parse_args()
 
 
-def source_digest():
-    h = hashlib.sha256()
-    for f in ("gemm.hip", "quantize.hip", "mx_device.h"):
-        with open(os.path.join(ROOT, "mxfp4_block_scaled_h16_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+class Plan:
+    """Buffers and the ordered launch list of one step (quantize and GEMM launches)."""
 
-
-def read_traffic(kernel, workload):
-    """HBM bytes per launch from a committed counter summary, if it matches the current sources."""
-    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.txt" % (kernel, workload))
-    if not os.path.exists(path):
-        return None
-    vals = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                vals[k.strip()] = v.strip()
-    if vals.get("source_digest") != source_digest():
-        return None
-    try:
-        return float(vals["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
-
-
-class Step:
-    """Preallocated buffers and the launch sequence of one Fprop + Dgrad + Wgrad step."""
-
-    def __init__(self, mx, torch, x, w, dy, M, K, N, h, sets):
-        self.mx, self.torch = mx, torch
-        self.M, self.K, self.N, self.h = M, K, N, h
-        dev = x.device
-        # rotate several copies of the inputs so consecutive steps do not hit in the 256 MB
-        # last-level cache
-        self.inputs = [(x, w, dy)] + [(x.clone(), w.clone(), dy.clone()) for _ in range(sets - 1)]
-        u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
-        self.fq = (u8(M, K // 2), u8(M, K // 32), u8(N, K // 2), u8(N, K // 32))
-        self.dq = (u8(M, N // 2), u8(M, N // 32), u8(K, N // 2), u8(K, N // 32))
-        self.wq = (u8(N, M // 2), u8(N, M // 32), u8(K, M // 2), u8(K, M // 32))
-        self.y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        self.dx = torch.empty((M, K), dtype=torch.float32, device=dev)
-        self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    def __init__(self, mx, torch, workload, h, sets):
+        import numpy as np
+        from synth import inputs
+        desc, projs, passes, M = WORKLOADS[workload]
+        self.mx, self.torch, self.h, self.passes, self.M = mx, torch, h, passes, M
         self.alpha = 1.0 / h if h else 1.0
-        self.i = 0
-        # launch list of one step: (name, callable)
-        self.names = ["quant_rows X", "quant_rows W", "gemm Fprop",
-                      "quant_rows dY", "quant_cols W", "gemm Dgrad",
-                      "quant_cols dY sr", "quant_cols X sr", "gemm Wgrad"]
+        dev = "cuda"
+        to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+        # host tensors (bf16 bit patterns), drawn by the shared seeded recipe
+        if workload == "layer":
+            acts, per_proj = inputs.llama_layer_inputs(seed=0, tokens=M)
+            self.host = {"acts": acts, "proj": per_proj}
+            inp = LLAMA_INPUT
+        else:
+            (name, K, N), = projs
+            if workload == "down":
+                dy, x = inputs.down_wgrad(seed=0, m=M, n=N, k=K)
+                w = inputs.weights(np.random.default_rng(1), N, K)
+            else:
+                x, w, dy = inputs.linear_inputs(M, K, N, seed=0)
+            acts, per_proj = {"x": x}, {name: (w, dy)}
+            self.host = {"acts": acts, "proj": per_proj}
+            inp = {name: "x"}
+        self.desc = desc
+        # device copies: `sets` rotated copies so consecutive steps do not hit in the 256 MB cache
+        self.sets = []
+        for s in range(sets):
+            d_acts = {k: to_dev(v) for k, v in acts.items()}
+            d_proj = {k: (to_dev(w), to_dev(dy)) for k, (w, dy) in per_proj.items()}
+            self.sets.append((d_acts, d_proj))
+        u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+        f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+        # quantized operand buffers (reused every step); contractions that are multiples of 512
+        # use the tiled layout, as the library's linear entry points do
+        self.q = {}
+        self.layout = {}
 
-    def launches(self):
-        mx, h = self.mx, self.h
-        x, w, dy = self.inputs[self.i % len(self.inputs)]
-        self.i += 1
-        fq, dq, wq = self.fq, self.dq, self.wq
-        return [
-            lambda: mx.quantize(x, 1, h, "rne", 0, 0, fq[0], fq[1]),
-            lambda: mx.quantize(w, 1, h, "rne", 0, 1, fq[2], fq[3]),
-            lambda: mx.gemm(fq[0], fq[1], fq[2], fq[3], self.alpha, self.y),
-            lambda: mx.quantize(dy, 1, h, "rne", 0, 0, dq[0], dq[1]),
-            lambda: mx.quantize(w, 0, h, "rne", 0, 1, dq[2], dq[3]),
-            lambda: mx.gemm(dq[0], dq[1], dq[2], dq[3], self.alpha, self.dx),
-            lambda: mx.quantize(dy, 0, h, "sr", 0x5EED, 0, wq[0], wq[1]),
-            lambda: mx.quantize(x, 0, h, "sr", 0x5EED, 1, wq[2], wq[3]),
-            lambda: mx.gemm(wq[0], wq[1], wq[2], wq[3], self.alpha, self.dw),
-        ]
+        def qbuf(key, outer, L):
+            tiled = L % 512 == 0
+            rows = -(-outer // 256) * 256 if tiled else outer
+            self.q[key] = (u8(rows, L // 2), u8(rows, L // 32))
+            self.layout[key] = "tiled" if tiled else "rows"
+        for a, x in acts.items():
+            K = x.shape[1]
+            if "F" in passes:
+                qbuf((a, "rows"), M, K)
+            if "W" in passes:
+                qbuf((a, "cols"), K, M)
+        self.out = {}
+        self.ops = []       # (label, kind, callable-builder, work) per launch; kind in quant/gemm
+        self.projs = projs
+        for name, K, N in projs:
+            a = inp[name]
+            if "F" in passes:
+                qbuf((name, "w_rows"), N, K)
+                self.out[(name, "F")] = f32(M, N)
+            if "D" in passes:
+                qbuf((name, "dy_rows"), M, N)
+                qbuf((name, "w_cols"), K, N)
+                self.out[(name, "D")] = f32(M, K)
+            if "W" in passes:
+                qbuf((name, "dy_cols"), N, M)
+                self.out[(name, "W")] = f32(N, K)
+        self._build(inp)
+
+    def _build(self, inp):
+        """Launch order: per activation its shared quantizations, then per projection its passes."""
+        M, h = self.M, self.h
+        ops = []
+        done = set()
+        for name, K, N in self.projs:
+            a = inp[name]
+            if "F" in self.passes and (a, "rows") not in done:
+                ops.append(("quant_rows %s" % a, "quant", ("act", a, 1, "rne", 0, 0, (a, "rows")), M * K))
+                done.add((a, "rows"))
+            if "W" in self.passes and (a, "cols") not in done:
+                ops.append(("quant_cols %s sr" % a, "quant", ("act", a, 0, "sr", 0x5EED, 1, (a, "cols")), M * K))
+                done.add((a, "cols"))
+            if "F" in self.passes:
+                ops.append(("quant_rows W_%s" % name, "quant", ("w", name, 1, "rne", 0, 1, (name, "w_rows")), N * K))
+                ops.append(("gemm Fprop %s" % name, "gemm", ((a, "rows"), (name, "w_rows"), (name, "F")), 2.0 * M * N * K))
+            if "D" in self.passes:
+                ops.append(("quant_rows dY_%s" % name, "quant", ("dy", name, 1, "rne", 0, 0, (name, "dy_rows")), M * N))
+                ops.append(("quant_cols W_%s" % name, "quant", ("w", name, 0, "rne", 0, 1, (name, "w_cols")), N * K))
+                ops.append(("gemm Dgrad %s" % name, "gemm", ((name, "dy_rows"), (name, "w_cols"), (name, "D")), 2.0 * M * N * K))
+            if "W" in self.passes:
+                ops.append(("quant_cols dY_%s sr" % name, "quant", ("dy", name, 0, "sr", 0x5EED, 0, (name, "dy_cols")), M * N))
+                ops.append(("gemm Wgrad %s" % name, "gemm", ((name, "dy_cols"), (a, "cols"), (name, "W")), 2.0 * M * N * K))
+        self.op_list = ops
+
+    def launches(self, step_index):
+        mx, h, alpha = self.mx, self.h, self.alpha
+        d_acts, d_proj = self.sets[step_index % len(self.sets)]
+        calls = []
+        for label, kind, spec, work in self.op_list:
+            if kind == "quant":
+                src, key, axis, rnd, seed, stream, dst = spec
+                t = d_acts[key] if src == "act" else d_proj[key][0 if src == "w" else 1]
+                q, s = self.q[dst]
+                calls.append(lambda t=t, axis=axis, rnd=rnd, seed=seed, stream=stream, q=q, s=s, lay=self.layout[dst]:
+                             mx.quantize(t, axis, h, rnd, seed, stream, q, s, layout=lay))
+            else:
+                qa, qb, out = spec
+                calls.append(lambda qa=self.q[qa], qb=self.q[qb], c=self.out[out], lay=self.layout[qa]:
+                             mx.gemm(qa[0], qa[1], qb[0], qb[1], alpha, c, layout=lay))
+        return calls
 
 
-def cpu_baseline(x, w, dy, M, K, N, h):
-    """The oracle, untuned, on a bounded sample of the same step; projected to the whole step."""
+def cpu_baseline(plan, h):
+    """The oracle, untuned, on a bounded sample of the same step, projected to the whole step."""
     import numpy as np
     import oracle
     threads = oracle.num_threads()
+    acts, per_proj = plan.host["acts"], plan.host["proj"]
+    # quantization rate: one sample per launch kind, about a second each
+    any_act = next(iter(acts.values()))
+    name0 = plan.projs[0][0]
+    w0, dy0 = per_proj[name0]
+    rows = min(any_act.shape[0], 256)
+    t0 = time.perf_counter()
+    oracle.quantize(np.ascontiguousarray(any_act[:rows]), 1, h, oracle.RNE)
+    rate_rows = rows * any_act.shape[1] / (time.perf_counter() - t0)
+    ncol = min(dy0.shape[1], 128)
+    sl = np.ascontiguousarray(dy0[:, :ncol])
+    t0 = time.perf_counter()
+    oracle.quantize(sl, 0, h, oracle.SR, seed=0x5EED)
+    rate_cols_sr = sl.size / (time.perf_counter() - t0)
+    ncolw = min(w0.shape[1], 128)
+    slw = np.ascontiguousarray(w0[:, :ncolw])
+    t0 = time.perf_counter()
+    oracle.quantize(slw, 0, h, oracle.RNE)
+    rate_cols = slw.size / (time.perf_counter() - t0)
     t_quant = 0.0
-    sample = []
-    # quantization rates, one slice per kind of launch in the step
-    n_rows = min(M, 512)
+    for label, kind, spec, work in plan.op_list:
+        if kind != "quant":
+            continue
+        axis, rnd = spec[2], spec[3]
+        rate = rate_rows if axis == 1 else (rate_cols_sr if rnd == "sr" else rate_cols)
+        t_quant += work / rate
+    # GEMM rate: 8 output rows of the first projection's Fprop-shaped product
+    qa = oracle.quantize(np.ascontiguousarray(any_act[:8]), 1, h, oracle.RNE)
+    qb = oracle.quantize(w0, 1, h, oracle.RNE, stream=1) if w0.shape[1] == any_act.shape[1] else None
+    if qb is None:
+        qa = oracle.quantize(np.ascontiguousarray(dy0[:8]), 1, h, oracle.RNE)
+        qb = oracle.quantize(w0, 0, h, oracle.RNE, stream=1)
     t0 = time.perf_counter()
-    oracle.quantize(x[:n_rows], 1, h, 0)
-    rate_rows = n_rows * K / (time.perf_counter() - t0)
-    n_cols = min(N, 256)
-    sl = np.ascontiguousarray(dy[:, :n_cols])
-    t0 = time.perf_counter()
-    oracle.quantize(sl, 0, h, 1, seed=0x5EED)
-    rate_cols_sr = M * n_cols / (time.perf_counter() - t0)
-    sl = np.ascontiguousarray(w[:, :n_cols]) if K >= n_cols else w
-    t0 = time.perf_counter()
-    oracle.quantize(sl, 0, h, 0)
-    rate_cols = sl.shape[0] * sl.shape[1] / (time.perf_counter() - t0)
-    sample.append("quantize: %d rows of X (rows, RNE), %d columns of dY (transposed, SR), %d columns "
-                  "of W (transposed, RNE)" % (n_rows, n_cols, sl.shape[1]))
-    t_quant = (M * K + N * K + M * N) / rate_rows + (N * K) / rate_cols + (M * N + M * K) / rate_cols_sr
-    # GEMM rate on whole output rows of each of the three GEMMs (operands quantized outside the clock)
-    rows = 16
-    flops, secs = 0.0, 0.0
-    for a_src, a_axis, b_src, b_axis, kc in ((x[:rows], 1, w, 1, K),
-                                             (dy[:rows], 1, w, 0, N),
-                                             (None, 0, x, 0, M)):
-        if a_src is None:
-            a = oracle.quantize(np.ascontiguousarray(dy[:, :rows]), 0, h, 1, seed=0x5EED)
-        else:
-            a = oracle.quantize(a_src, a_axis, h, 0)
-        b = oracle.quantize(b_src, b_axis, h, 1 if a_src is None else 0, seed=0x5EED, stream=1)
-        t0 = time.perf_counter()
-        c = oracle.gemm(*a, *b, alpha=1.0 / h if h else 1.0)
-        secs += time.perf_counter() - t0
-        flops += 2.0 * c.shape[0] * c.shape[1] * kc
-    rate_gemm = flops / secs
-    sample.append("GEMM: %d output rows of each of Fprop, Dgrad, Wgrad (%.2f GFLOP)" % (rows, flops / 1e9))
-    step_flops = 3 * 2.0 * M * N * K
+    c = oracle.gemm(*qa, *qb, alpha=oracle.alpha_for(h))
+    secs = time.perf_counter() - t0
+    rate_gemm = 2.0 * c.shape[0] * c.shape[1] * qa[0].shape[1] * 2 / secs
+    step_flops = sum(work for label, kind, spec, work in plan.op_list if kind == "gemm")
     t_step = t_quant + step_flops / rate_gemm
     return {"value": step_flops / t_step / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "; ".join(sample) + "; projected to the whole step",
+            "sample": ("quantize %d rows (RNE, along rows), %d columns of dY (transposed, SR), %d columns of W "
+                       "(transposed, RNE); GEMM 8 output rows of %s; projected to the whole step"
+                       % (rows, ncol, ncolw, name0)),
             "gemm_gflops": rate_gemm / 1e9, "quantize_melem_s": rate_rows / 1e6,
             "step_seconds_projected": t_step}
 
@@ -178,33 +230,33 @@ def main():
     import numpy as np
     import torch
     import mxfp4_block_scaled_h16_amd as mx
-    from synth import inputs
 
-    M, K, N, desc = WORKLOADS[args.workload]
     h = args.hadamard
-    xh, wh, dyh = inputs.linear_inputs(M, K, N, seed=0)
-    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
-    x, w, dy = to_dev(xh), to_dev(wh), to_dev(dyh)
-    in_bytes = 2 * (M * K + N * K + M * N)
+    desc, projs, passes, M = WORKLOADS[args.workload]
+    in_bytes = 0
+    for name, K, N in projs:
+        in_bytes += 2 * (N * K + M * N)
+    in_bytes += 2 * M * sum(K for name, K, N in projs)
     sets = max(1, min(8, -(-(1 << 30) // in_bytes)))
-    step = Step(mx, torch, x, w, dy, M, K, N, h, sets)
+    plan = Plan(mx, torch, args.workload, h, sets)
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
-        for f in step.launches():
+    for s in range(args.warmup):
+        for f in plan.launches(s):
             f()
     torch.cuda.synchronize()
 
     # timed region: K steps, per-launch HIP events on the stream the kernels run on
     stream = torch.cuda.current_stream()
-    n_launch = len(step.names)
+    n_launch = len(plan.op_list)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)] for _ in range(args.steps)]
+    calls = [plan.launches(s) for s in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         ev = events[s]
         ev[0].record(stream)
-        for i, f in enumerate(step.launches()):
+        for i, f in enumerate(calls[s]):
             f()
             ev[i + 1].record(stream)
     torch.cuda.synchronize()
@@ -214,34 +266,31 @@ def main():
     per_launch = np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(n_launch)]
                            for s in range(args.steps)])  # ms
     avg_ms = per_launch.mean(0)
-    gemm_flops = 2.0 * M * N * K
-    step_flops = 3 * gemm_flops
+    step_flops = sum(w for _, kind, _, w in plan.op_list if kind == "gemm")
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     kernels = {}
-    quant_elems = [M * K, N * K, None, M * N, N * K, None, M * N, M * K, None]
-    for name, t, e in zip(step.names, avg_ms, quant_elems):
+    gemm_flops, gemm_s, q_bytes, q_s = 0.0, 0.0, 0.0, 0.0
+    for (label, kind, spec, work), t in zip(plan.op_list, avg_ms):
         entry = {"us": round(float(t) * 1e3, 2)}
-        if e is None:
-            entry["tflops"] = round(gemm_flops / (t * 1e-3) / 1e12, 1)
+        if kind == "gemm":
+            entry["tflops"] = round(work / (t * 1e-3) / 1e12, 1)
+            gemm_flops += work
+            gemm_s += float(t) * 1e-3
         else:
-            entry["gbs"] = round(e * QUANT_BYTES_PER_ELEM / (t * 1e-3) / 1e9, 1)
-        kernels[name] = entry
+            entry["gbs"] = round(work * QUANT_BYTES_PER_ELEM / (t * 1e-3) / 1e9, 1)
+            q_bytes += work * QUANT_BYTES_PER_ELEM
+            q_s += float(t) * 1e-3
+        kernels[label] = entry
 
-    gemm_idx = [2, 5, 8]
-    gemm_avg_s = float(avg_ms[gemm_idx].mean()) * 1e-3
-    achieved = gemm_flops / gemm_avg_s / 1e12
-    traffic = read_traffic("gemm", args.workload)
+    n_gemm = sum(1 for _, kind, _, _ in plan.op_list if kind == "gemm")
+    achieved = gemm_flops / gemm_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MXFP4_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MXFP4_PEAK_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_mxfp4 (average over the step's Fprop, Dgrad and Wgrad launches)",
-                "algorithmic_per_launch": "2*M*N*K = %.1f GFLOP" % (gemm_flops / 1e9)}
-
-    q_idx = [0, 1, 3, 4, 6, 7]
-    q_bytes = sum(quant_elems[i] for i in q_idx) * QUANT_BYTES_PER_ELEM
-    q_time = float(sum(avg_ms[i] for i in q_idx)) * 1e-3
-    quantizer = {"gbs": round(q_bytes / q_time / 1e9, 1), "frac_of_hbm": round(q_bytes / q_time / 1e9 / HBM_PEAK_GBS, 4),
-                 "bytes_per_elem": QUANT_BYTES_PER_ELEM, "us_per_step": round(q_time * 1e6, 1)}
+                "unit": "TFLOP/s", "frac": round(achieved / MXFP4_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_mxfp4_pipelined (%d launches per step; achieved = GEMM FLOPs / GEMM time)" % n_gemm,
+                "algorithmic_per_launch": "2*M*N*K = %.1f GFLOP average" % (gemm_flops / n_gemm / 1e9)}
+    quantizer = {"gbs": round(q_bytes / q_s / 1e9, 1), "frac_of_hbm": round(q_bytes / q_s / 1e9 / HBM_PEAK_GBS, 4),
+                 "bytes_per_elem": QUANT_BYTES_PER_ELEM, "us_per_step": round(q_s * 1e6, 1)}
 
     if args.copy_calibration:
         buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -249,20 +298,18 @@ def main():
         buf2.copy_(buf)
         torch.cuda.synchronize()
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(xh, wh, dyh, M, K, N, h)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(plan, h)
 
+    sizes = ", ".join("%s K=%d N=%d" % (n, k, nn) for n, k, nn in projs)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
         "data": "synthetic",
-        "config": {"workload": "%s Fprop+Dgrad+Wgrad, M=%d tokens, K=%d, N=%d, H%d, MXFP4 RNE "
-                               "(SR on Wgrad operands)" % (desc, M, K, N, h),
-                   "M": M, "K": K, "N": N, "hadamard": h, "input_sets": sets},
+        "config": {"workload": "%s, M=%d tokens, %s, H%d, MXFP4 RNE (Philox SR on Wgrad operands)"
+                               % (desc, M, sizes, h),
+                   "M": M, "hadamard": h, "passes": passes, "input_sets": sets},
         "roofline": roofline, "quantizer": quantizer, "kernels": kernels, "cpu_baseline": cpu,
-        "source_digest": source_digest(),
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 1
+#define MXFP4_ABI_VERSION 2
 
 typedef enum {
     MXFP4_OK = 0,
@@ -70,6 +70,28 @@ typedef enum { MXFP4_RNE = 0, MXFP4_SR_PHILOX = 1 } mxfp4_rounding_t;
 typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
 
 /*
+ * Memory layout of a quantized operand with `outer` quantized rows of length L.
+ *
+ * MXFP4_LAYOUT_ROWS: row-major. codes q[outer][ldq] bytes (the first L/2 used: element j of row o
+ *   is nibble j % 2 of byte j / 2, even element in the low nibble), scales s[outer][lds] bytes
+ *   (the first L/32 used: block c covers elements [32 c, 32 c + 32)).
+ * MXFP4_LAYOUT_TILED: the layout the GEMM streams without reshuffling; requires L % 512 == 0.
+ *   Rows are padded to R = 256 * ceil(outer / 256); the padding is never written and only feeds
+ *   outputs that are discarded. With the same nibble packing inside each 16-byte chunk:
+ *     codes (R * L / 2 bytes): the chunk holding block c of row o starts at byte
+ *       ((o / 16) * (L / 128) + c / 4) * 1024 + (o % 16) * 64 + 16 * ((c % 4) ^ ((o % 16) / 4));
+ *     scales (R * L / 32 bytes): the scale of block c of row o is byte
+ *       ((o / 64) * (L / 512) + c / 16) * 1024 + (o % 64) * 16 + (c % 16).
+ *   Every 16-row x 128-element slice of codes and every 64-row x 512-element slice of scales is
+ *   one contiguous kilobyte. Both pointers must be 16-byte aligned; ldq and lds are not used.
+ */
+typedef enum { MXFP4_LAYOUT_ROWS = 0, MXFP4_LAYOUT_TILED = 1 } mxfp4_layout_t;
+
+/* Bytes of codes and of scales of a tiled operand (outer rows, length L); MXFP4_ERR_SHAPE if
+ * L % 512 != 0 or a size is negative, MXFP4_ERR_NULL if an output pointer is NULL. */
+mxfp4_status_t mxfp4_tiled_sizes(int64_t outer, int64_t L, size_t *codes_bytes, size_t *scales_bytes);
+
+/*
  * mxfp4_quantize -- rotate then quantize a 2-D tensor to MXFP4.
  *
  * Defined by: the operand transform of the Methodology section (deterministic H16/H32 rotation,
@@ -82,16 +104,18 @@ typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
  *                                                  q[cols][ldq], scales[cols][lds]
  *            (the Wgrad token axis and the Dgrad weight operand).
  *   hadamard 0 (no rotation), 16 or 32; rounding MXFP4_RNE or MXFP4_SR_PHILOX with (seed, stream).
+ *   layout   MXFP4_LAYOUT_ROWS (q, ldq, scales, lds as above) or MXFP4_LAYOUT_TILED (see above).
  *
  * Requirements: rows, cols >= 0; L % 32 == 0; at most 2^30 32-element blocks (rows * cols / 32);
- * ldx >= cols; ldq >= L/2; lds >= L/32.
+ * rows layout: ldx >= cols; ldq >= L/2; lds >= L/32. Tiled layout: L % 512 == 0.
  * Alignment: x 16-byte aligned and ldx * sizeof(element) a multiple of 16; q 16-byte aligned and
- * ldq % 16 == 0. Empty tensors return MXFP4_OK without a launch.
+ * (rows layout) ldq % 16 == 0; (tiled layout) scales 16-byte aligned. Empty tensors return
+ * MXFP4_OK without a launch.
  */
 mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
                               int64_t ldx, int axis, int hadamard, mxfp4_rounding_t rounding,
-                              uint64_t seed, uint32_t stream_id, uint8_t *q, int64_t ldq,
-                              uint8_t *scales, int64_t lds, void *stream);
+                              uint64_t seed, uint32_t stream_id, mxfp4_layout_t layout, uint8_t *q,
+                              int64_t ldq, uint8_t *scales, int64_t lds, void *stream);
 
 /*
  * mxfp4_gemm -- block-scaled FP4 GEMM with FP32 accumulation and output.
@@ -101,13 +125,15 @@ mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
  * with A = (aq [M][lda bytes], as [M][ldas bytes]) and B = (bq [N][ldb], bs [N][ldbs]) both
  * quantized along K (the layout mxfp4_quantize writes), deq(code, S) = e2m1(code) * 2^(S-127).
  * Any 0xFF scale in the contributing blocks makes the output NaN.
- * c is FP32 [M][ldc] (device). Requirements: M, N, K >= 0, K % 32 == 0, lda, ldb >= K/2 and
- * multiples of 16, ldas, ldbs >= K/32, ldc >= N; aq, bq 16-byte aligned.
+ * c is FP32 [M][ldc] (device). Requirements: M, N, K >= 0, K % 32 == 0, ldc >= N. Rows layout:
+ * lda, ldb >= K/2 and multiples of 16, ldas, ldbs >= K/32, aq, bq 16-byte aligned. Tiled layout
+ * (both operands, as mxfp4_quantize writes it with L = K): K % 512 == 0, all four operand
+ * pointers 16-byte aligned, the leading dimensions unused.
  */
 mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
                           int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,
-                          void *stream);
+                          mxfp4_layout_t layout, void *stream);
 
 /* Per-operand configuration of one linear-layer GEMM. */
 typedef struct {

@@ -15,7 +15,8 @@ import torch  # imported first: the library binds to the HIP runtime torch has l
 
 __all__ = [
     "Mxfp4Error", "quantize", "gemm", "linear_fprop", "linear_dgrad", "linear_wgrad",
-    "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
+    "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD", "ROWS", "TILED",
+    "tiled_sizes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,6 +24,7 @@ _LIB_PATH = os.path.join(_HERE, "libmxfp4.so")
 
 RNE, SR = 0, 1
 FPROP, DGRAD, WGRAD = 0, 1, 2
+ROWS, TILED = 0, 1
 BF16, F32 = 0, 1
 
 _lib = None
@@ -53,10 +55,13 @@ def lib():
                           "(or __graft_entry__.build())" % _LIB_PATH)
     L = ctypes.CDLL(_LIB_PATH)
     i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
-    L.mxfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, u64, u32, vp, i64, vp, i64, vp]
+    L.mxfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, u64, u32, ci, vp, i64, vp, i64, vp]
     L.mxfp4_quantize.restype = ci
-    L.mxfp4_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64, vp]
+    L.mxfp4_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64,
+                             ci, vp]
     L.mxfp4_gemm.restype = ci
+    L.mxfp4_tiled_sizes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    L.mxfp4_tiled_sizes.restype = ci
     L.mxfp4_linear_workspace_bytes.argtypes = [ci, i64, i64, i64]
     L.mxfp4_linear_workspace_bytes.restype = ctypes.c_size_t
     for name in ("mxfp4_linear_fprop", "mxfp4_linear_dgrad", "mxfp4_linear_wgrad"):
@@ -99,18 +104,35 @@ def _rounding(r):
     raise ValueError("rounding must be 'rne' or 'sr'")
 
 
+def _layout(layout):
+    if layout in (ROWS, "rows"):
+        return ROWS
+    if layout in (TILED, "tiled"):
+        return TILED
+    raise ValueError("layout must be 'rows' or 'tiled'")
+
+
+def tiled_sizes(outer, L):
+    """(codes bytes, scales bytes) of a tiled operand with `outer` rows of length L."""
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().mxfp4_tiled_sizes(int(outer), int(L), ctypes.byref(cb), ctypes.byref(sb)), "mxfp4_tiled_sizes")
+    return cb.value, sb.value
+
+
 def _require_cuda(t, name):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError("%s must be a tensor on a HIP device" % name)
 
 
 def quantize(x, axis=1, hadamard=16, rounding="rne", seed=0, stream_id=0, q=None, scales=None,
-             stream=None):
+             stream=None, layout="rows"):
     """Rotate then quantize a 2-D bf16/f32 device tensor to MXFP4.
 
-    Returns (q uint8 [outer, L/2], scales uint8 [outer, L/32]); axis=0 gives the quantized
-    transpose (outer = columns).
+    Returns (q, scales) uint8 tensors. Row layout: q [outer, L/2], scales [outer, L/32]; axis=0
+    gives the quantized transpose (outer = columns). Tiled layout: the same bytes per row but rows
+    padded to a multiple of 256 and arranged as include/mxfp4.h describes.
     """
+    lay = _layout(layout)
     _require_cuda(x, "x")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
@@ -119,29 +141,37 @@ def quantize(x, axis=1, hadamard=16, rounding="rne", seed=0, stream_id=0, q=None
         raise TypeError("x must be bfloat16 or float32")
     rows, cols = x.shape
     L, outer = (cols, rows) if axis == 1 else (rows, cols)
+    padded = (outer + 255) // 256 * 256 if lay == TILED else outer
     if q is None:
-        q = torch.empty((outer, L // 2), dtype=torch.uint8, device=x.device)
+        q = torch.empty((padded, L // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((outer, L // 32), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((padded, L // 32), dtype=torch.uint8, device=x.device)
     st = lib().mxfp4_quantize(x.data_ptr(), dtype, rows, cols, x.stride(0), axis, hadamard,
-                              _rounding(rounding), int(seed) & (2 ** 64 - 1), int(stream_id),
-                              q.data_ptr(), q.stride(0), scales.data_ptr(), scales.stride(0),
-                              _stream(stream))
+                              _rounding(rounding), int(seed) & (2 ** 64 - 1), int(stream_id), lay,
+                              q.data_ptr(), q.stride(0) if q.dim() == 2 else 0, scales.data_ptr(),
+                              scales.stride(0) if scales.dim() == 2 else 0, _stream(stream))
     _check(st, "mxfp4_quantize")
     return q, scales
 
 
-def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None):
-    """c[m][n] = alpha * sum_k deq(A)[m][k] deq(B)[n][k] (FP32 [M, N])."""
-    for t, n in ((aq, "aq"), (as_, "as"), (bq, "bq"), (bs, "bs")):
-        _require_cuda(t, n)
+def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None, layout="rows", m=None, n=None):
+    """c[m][n] = alpha * sum_k deq(A)[m][k] deq(B)[n][k] (FP32 [M, N]).
+
+    Tiled operands are padded to 256 rows, so M and N come from `out`, or `m` and `n`."""
+    lay = _layout(layout)
+    for t, nm in ((aq, "aq"), (as_, "as"), (bq, "bq"), (bs, "bs")):
+        _require_cuda(t, nm)
     M, K = aq.shape[0], aq.shape[1] * 2
     N = bq.shape[0]
+    if out is not None:
+        M, N = out.shape
+    M = M if m is None else int(m)
+    N = N if n is None else int(n)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=aq.device)
     st = lib().mxfp4_gemm(aq.data_ptr(), aq.stride(0), as_.data_ptr(), as_.stride(0), bq.data_ptr(),
                           bq.stride(0), bs.data_ptr(), bs.stride(0), M, N, K, float(alpha),
-                          out.data_ptr(), out.stride(0), _stream(stream))
+                          out.data_ptr(), out.stride(0), lay, _stream(stream))
     _check(st, "mxfp4_gemm")
     return out
 

@@ -2,6 +2,8 @@
 // Every argument check happens before the first HIP call, so an invalid call launches nothing,
 // touches no output and needs no device.
 #include <atomic>
+#include <climits>
+#include <cstdint>
 #include <cstring>
 
 #include "../../include/mxfp4.h"
@@ -36,8 +38,11 @@ mxfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP
 // Validation of one quantize call; also used by the linear entry points.
 mxfp4_status_t check_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
                               int64_t ldx, int axis, int hadamard, mxfp4_rounding_t rounding,
-                              const uint8_t *q, int64_t ldq, const uint8_t *scales, int64_t lds)
+                              mxfp4_layout_t layout, const uint8_t *q, int64_t ldq,
+                              const uint8_t *scales, int64_t lds)
 {
+    if (layout != MXFP4_LAYOUT_ROWS && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_ARG;
+    const bool tiled = layout == MXFP4_LAYOUT_TILED;
     if (dtype != MXFP4_IN_BF16 && dtype != MXFP4_IN_F32) return MXFP4_ERR_ARG;
     if (axis != 0 && axis != 1) return MXFP4_ERR_ARG;
     if (hadamard != 0 && hadamard != 16 && hadamard != 32) return MXFP4_ERR_ARG;
@@ -45,38 +50,53 @@ mxfp4_status_t check_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
     if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return MXFP4_ERR_SHAPE;
     const int64_t L = axis ? cols : rows;
     const int64_t outer = axis ? rows : cols;
-    if (L % 32 != 0) return MXFP4_ERR_SHAPE;
+    if (L % (tiled ? 512 : 32) != 0) return MXFP4_ERR_SHAPE;
     if (outer > 0 && L / 32 > 0 && outer > kMaxBlocks / (L / 32)) return MXFP4_ERR_SHAPE;
-    if (ldx < cols || ldx < 1 || ldq < L / 2 || lds < L / 32) return MXFP4_ERR_ARG;
+    if (ldx < cols || ldx < 1) return MXFP4_ERR_ARG;
+    if (!tiled && (ldq < L / 2 || lds < L / 32)) return MXFP4_ERR_ARG;
     if (rows == 0 || cols == 0) return MXFP4_OK;
     if (!x || !q || !scales) return MXFP4_ERR_NULL;
     const int64_t esize = dtype == MXFP4_IN_F32 ? 4 : 2;
     if (!aligned(x, 16) || (ldx * esize) % 16 != 0) return MXFP4_ERR_ALIGN;
-    if (!aligned(q, 16) || ldq % 16 != 0) return MXFP4_ERR_ALIGN;
+    if (!aligned(q, 16)) return MXFP4_ERR_ALIGN;
+    if (tiled ? !aligned(scales, 16) : ldq % 16 != 0) return MXFP4_ERR_ALIGN;
     return MXFP4_OK;
 }
 
+int64_t pad256(int64_t v) { return (v + 255) / 256 * 256; }
+
 mxfp4_status_t check_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
-                          int64_t M, int64_t N, int64_t K, const float *c, int64_t ldc)
+                          int64_t M, int64_t N, int64_t K, const float *c, int64_t ldc,
+                          mxfp4_layout_t layout)
 {
+    if (layout != MXFP4_LAYOUT_ROWS && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_ARG;
+    const bool tiled = layout == MXFP4_LAYOUT_TILED;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MXFP4_ERR_SHAPE;
-    if (K % 32 != 0) return MXFP4_ERR_SHAPE;
-    if (lda < K / 2 || ldb < K / 2 || ldas < K / 32 || ldbs < K / 32 || ldc < N || ldc < 1)
-        return MXFP4_ERR_ARG;
+    if (K % (tiled ? 512 : 32) != 0) return MXFP4_ERR_SHAPE;
+    // tiled operands are addressed with 32-bit byte offsets
+    if (tiled && (pad256(M) * (K / 2) > (int64_t)UINT32_MAX || pad256(N) * (K / 2) > (int64_t)UINT32_MAX))
+        return MXFP4_ERR_SHAPE;
+    if (ldc < N || ldc < 1) return MXFP4_ERR_ARG;
+    if (!tiled && (lda < K / 2 || ldb < K / 2 || ldas < K / 32 || ldbs < K / 32)) return MXFP4_ERR_ARG;
     if (M == 0 || N == 0) return MXFP4_OK;
     if (!c) return MXFP4_ERR_NULL;
     if (K > 0 && (!aq || !as || !bq || !bs)) return MXFP4_ERR_NULL;
-    if (!aligned(aq, 16) || !aligned(bq, 16) || lda % 16 != 0 || ldb % 16 != 0) return MXFP4_ERR_ALIGN;
+    if (!aligned(aq, 16) || !aligned(bq, 16)) return MXFP4_ERR_ALIGN;
+    if (tiled ? (!aligned(as, 16) || !aligned(bs, 16)) : (lda % 16 != 0 || ldb % 16 != 0))
+        return MXFP4_ERR_ALIGN;
     if (!aligned(c, 4)) return MXFP4_ERR_ALIGN;
     return MXFP4_OK;
 }
 
 // Workspace layout of one linear call: A codes | A scales | B codes | B scales, each 256-aligned.
+// Contractions that are multiples of 512 use the tiled layout (rows padded to 256).
 struct OperandSpace {
     int64_t outer, L;
-    size_t codes() const { return (size_t)outer * (size_t)(L / 2); }
-    size_t scales() const { return (size_t)outer * (size_t)(L / 32); }
+    bool tiled() const { return L > 0 && L % 512 == 0; }
+    int64_t rows() const { return tiled() ? pad256(outer) : outer; }
+    size_t codes() const { return (size_t)rows() * (size_t)(L / 2); }
+    size_t scales() const { return (size_t)rows() * (size_t)(L / 32); }
 };
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -117,6 +137,8 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     pass_operands(pass, M, K, N, &a, &b);
     if (a.outer > 0 && a.L / 32 > 0 && (a.outer > kMaxBlocks / (a.L / 32) || b.outer > kMaxBlocks / (a.L / 32)))
         return MXFP4_ERR_SHAPE;
+    const bool tiled = a.tiled();
+    if (tiled && (a.codes() > UINT32_MAX || b.codes() > UINT32_MAX)) return MXFP4_ERR_SHAPE;
     if (sp.out_rows == 0 || sp.out_cols == 0) return MXFP4_OK;
     if (!out) return MXFP4_ERR_NULL;
     if (!aligned(out, 4)) return MXFP4_ERR_ALIGN;
@@ -145,16 +167,17 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
                      uint32_t sid, uint8_t *q, uint8_t *sc, int64_t L) {
         if (axis == 1)
             return mx::launch_quantize_rows(src, false, rows, cols, cols, cfg->hadamard,
-                                            rnd == MXFP4_SR_PHILOX, cfg->seed, sid, q, L / 2, sc,
-                                            L / 32, s);
+                                            rnd == MXFP4_SR_PHILOX, cfg->seed, sid, tiled, q, L / 2,
+                                            sc, L / 32, s);
         return mx::launch_quantize_cols(src, false, rows, cols, cols, cfg->hadamard,
-                                        rnd == MXFP4_SR_PHILOX, cfg->seed, sid, q, L / 2, sc, L / 32, s);
+                                        rnd == MXFP4_SR_PHILOX, cfg->seed, sid, tiled, q, L / 2, sc,
+                                        L / 32, s);
     };
     hipError_t e = quant(sp.a_src, sp.a_rows, sp.a_cols, sp.a_axis, cfg->rnd_a, 0u, aq, as, a.L);
     if (e == hipSuccess) e = quant(sp.b_src, sp.b_rows, sp.b_cols, sp.b_axis, cfg->rnd_b, 1u, bq, bs, b.L);
     if (e == hipSuccess)
         e = mx::launch_gemm(aq, a.L / 2, as, a.L / 32, bq, b.L / 2, bs, b.L / 32, sp.out_rows,
-                            sp.out_cols, sp.kc, alpha, out, sp.out_cols, s);
+                            sp.out_cols, sp.kc, alpha, out, sp.out_cols, tiled, s);
     return from_hip(e);
 }
 
@@ -164,29 +187,30 @@ extern "C" {
 
 mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
                               int64_t ldx, int axis, int hadamard, mxfp4_rounding_t rounding,
-                              uint64_t seed, uint32_t stream_id, uint8_t *q, int64_t ldq,
-                              uint8_t *scales, int64_t lds, void *stream)
+                              uint64_t seed, uint32_t stream_id, mxfp4_layout_t layout, uint8_t *q,
+                              int64_t ldq, uint8_t *scales, int64_t lds, void *stream)
 {
-    mxfp4_status_t st = check_quantize(x, dtype, rows, cols, ldx, axis, hadamard, rounding, q, ldq,
-                                       scales, lds);
+    mxfp4_status_t st = check_quantize(x, dtype, rows, cols, ldx, axis, hadamard, rounding, layout,
+                                       q, ldq, scales, lds);
     if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
     if ((st = check_device()) != MXFP4_OK) return st;
     const bool f32 = dtype == MXFP4_IN_F32;
     const bool sr = rounding == MXFP4_SR_PHILOX;
+    const bool tiled = layout == MXFP4_LAYOUT_TILED;
     hipError_t e = axis == 1
-        ? mx::launch_quantize_rows(x, f32, rows, cols, ldx, hadamard, sr, seed, stream_id, q, ldq,
-                                   scales, lds, (hipStream_t)stream)
-        : mx::launch_quantize_cols(x, f32, rows, cols, ldx, hadamard, sr, seed, stream_id, q, ldq,
-                                   scales, lds, (hipStream_t)stream);
+        ? mx::launch_quantize_rows(x, f32, rows, cols, ldx, hadamard, sr, seed, stream_id, tiled, q,
+                                   ldq, scales, lds, (hipStream_t)stream)
+        : mx::launch_quantize_cols(x, f32, rows, cols, ldx, hadamard, sr, seed, stream_id, tiled, q,
+                                   ldq, scales, lds, (hipStream_t)stream);
     return from_hip(e);
 }
 
 mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
                           int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,
-                          void *stream)
+                          mxfp4_layout_t layout, void *stream)
 {
-    mxfp4_status_t st = check_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, c, ldc);
+    mxfp4_status_t st = check_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, c, ldc, layout);
     if (st != MXFP4_OK || M == 0 || N == 0) return st;
     if ((st = check_device()) != MXFP4_OK) return st;
     if (K == 0) {
@@ -194,7 +218,16 @@ mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int
         return from_hip(mx::launch_fill_zero(c, M, N, ldc, (hipStream_t)stream));
     }
     return from_hip(mx::launch_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, alpha, c, ldc,
-                                    (hipStream_t)stream));
+                                    layout == MXFP4_LAYOUT_TILED, (hipStream_t)stream));
+}
+
+mxfp4_status_t mxfp4_tiled_sizes(int64_t outer, int64_t L, size_t *codes_bytes, size_t *scales_bytes)
+{
+    if (!codes_bytes || !scales_bytes) return MXFP4_ERR_NULL;
+    if (outer < 0 || L < 0 || outer > kMaxDim || L > kMaxDim || L % 512 != 0) return MXFP4_ERR_SHAPE;
+    *codes_bytes = (size_t)pad256(outer) * (size_t)(L / 2);
+    *scales_bytes = (size_t)pad256(outer) * (size_t)(L / 32);
+    return MXFP4_OK;
 }
 
 size_t mxfp4_linear_workspace_bytes(mxfp4_pass_t pass, int64_t M, int64_t K, int64_t N)

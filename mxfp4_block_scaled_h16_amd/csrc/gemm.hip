@@ -134,9 +134,7 @@ constexpr int kScaleSlot = (kBM + kBN) * 16;          // 8 KB: 16 scale bytes pe
 constexpr int kScaleBase = kNumBuf * kStageBytes;     // two scale slots after the stage ring
 constexpr int kLdsBytes = kScaleBase + 2 * kScaleSlot;  // 144 KB
 constexpr int kRowsPerDma = 1024 / kRowBytes;         // one wave-wide 16 B/lane DMA covers 16 rows
-constexpr int kDmaPerOperand = kBM / kRowsPerDma / 4; // 4 per operand per wavefront
-constexpr int kDmaPerStage = 2 * kDmaPerOperand;      // 8 VMEM instructions per wavefront
-constexpr int kDmaPerScales = 2;                      // 1 per operand per wavefront per group
+constexpr int kGemmWaves = 4;                         // wavefronts per workgroup (4 or 8)
 
 __device__ __forceinline__ int chunk_perm(int row) { return (row >> 2) & 3; }
 
@@ -158,20 +156,26 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-struct PipeCtx {
-    const uint8_t *aq, *bq, *as, *bs;
-    uint32_t a_off[kDmaPerOperand], b_off[kDmaPerOperand];  // per-lane code offsets
-    uint32_t as_off, bs_off;                                 // per-lane scale offsets
-    int dma_row0;                                            // first stage row of this wave's DMA
-    int a_frag, b_frag, chunk0, chunk1;                      // fragment read offsets
-    int sa_lds, sb_lds;                                      // scale word offsets (stage 0)
+// Geometry of the pipelined kernel with NW wavefronts: a 2 x (NW / 2) arrangement of wave tiles
+// of 128 rows (four 32-row MFMA tiles of A) by 512 / NW columns (FJ 32-column tiles of B).
+template <int NW>
+struct Geo {
+    static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts");
+    static constexpr int kWaveCols = 512 / NW;
+    static constexpr int FI = 4, FJ = kWaveCols / 32;
+    static constexpr int kDmaPerOperand = kBM / kRowsPerDma / NW;  // per wavefront and stage
+    static constexpr int kDmaPerStage = 2 * kDmaPerOperand;
+    static constexpr int kDmaPerScales = 8 / NW;                    // per wavefront and group
 };
 
-__global__ __launch_bounds__(256, 1) void gemm_mxfp4_pipelined(
+template <int NW, bool TILED>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
     int M, int N, int K, float alpha, float *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n)
 {
+    using G = Geo<NW>;
+    constexpr int FI = G::FI, FJ = G::FJ;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
     // tile order: consecutive workgroups are spread over the 8 XCDs; give each XCD a contiguous
@@ -189,112 +193,140 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_pipelined(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave & 1, wn = wave >> 1;
     const int r = lane & 31, half = lane >> 5;
 
-    PipeCtx p;
-    p.aq = aq;
-    p.bq = bq;
-    p.as = as;
-    p.bs = bs;
-    // code DMA: instruction u of this wavefront fills stage rows [16 (4 wave + u), + 16) of each
-    // operand; lane L writes the 16 bytes at row + L / 4, physical chunk L % 4
-    p.dma_row0 = kRowsPerDma * kDmaPerOperand * wave;
+    // code DMA: instruction u of this wavefront fills stage rows [16 (kDmaPerOperand wave + u),
+    // + 16) of each operand; lane L writes the 16 bytes at row + L / 4, physical chunk L % 4.
+    // Row-major operands: lane L reads its row's logical chunk (L % 4) ^ perm(row). Tiled operands
+    // already hold each 16-row x 128-K block as those 1024 bytes, in that order.
+    const int dma_row0 = kRowsPerDma * G::kDmaPerOperand * wave;
+    const int kblocks = K / kStageK;
+    uint32_t a_off[G::kDmaPerOperand], b_off[G::kDmaPerOperand];
 #pragma unroll
-    for (int u = 0; u < kDmaPerOperand; ++u) {
-        const int row = p.dma_row0 + kRowsPerDma * u + lane / 4;
-        const int chunk = (lane % 4) ^ chunk_perm(row);
-        p.a_off[u] = (uint32_t)(min(m0 + row, M - 1) * lda + 16 * chunk);
-        p.b_off[u] = (uint32_t)(min(n0 + row, N - 1) * ldb + 16 * chunk);
+    for (int u = 0; u < G::kDmaPerOperand; ++u) {
+        if constexpr (TILED) {
+            const int rb = (dma_row0 + kRowsPerDma * u) / 16;
+            a_off[u] = (uint32_t)((m0 / 16 + rb) * kblocks * 1024 + lane * 16);
+            b_off[u] = (uint32_t)((n0 / 16 + rb) * kblocks * 1024 + lane * 16);
+        } else {
+            const int row = dma_row0 + kRowsPerDma * u + lane / 4;
+            const int chunk = (lane % 4) ^ chunk_perm(row);
+            a_off[u] = (uint32_t)(min(m0 + row, M - 1) * lda + 16 * chunk);
+            b_off[u] = (uint32_t)(min(n0 + row, N - 1) * ldb + 16 * chunk);
+        }
     }
-    // scale DMA: wavefront w brings rows [64 w, 64 w + 64) of each operand, 16 bytes per lane
-    p.as_off = (uint32_t)(min(m0 + 64 * wave + lane, M - 1) * ldas);
-    p.bs_off = (uint32_t)(min(n0 + 64 * wave + lane, N - 1) * ldbs);
+    // scale DMA: 64 rows of one operand per instruction, 16 bytes (one group) per lane; with 4
+    // wavefronts each brings rows [64 w, + 64) of both operands, with 8 wavefront w < 4 brings
+    // A rows [64 w, + 64) and wavefront w >= 4 B rows [64 (w - 4), + 64)
+    uint32_t s_off[G::kDmaPerScales];
+    int s_dst[G::kDmaPerScales];
+    const uint8_t *s_src[G::kDmaPerScales];
+#pragma unroll
+    for (int u = 0; u < G::kDmaPerScales; ++u) {
+        const bool is_b = NW == 4 ? u == 1 : wave >= 4;
+        const int row = 64 * (NW == 4 ? wave : (wave & 3)) + lane;
+        s_src[u] = is_b ? bs : as;
+        if constexpr (TILED) {
+            // 64-row x 512-K scale blocks of 1024 bytes, 16 per row
+            const int q64 = (NW == 4 ? wave : (wave & 3));
+            s_off[u] = (uint32_t)(((is_b ? n0 : m0) / 64 + q64) * (K / 512) * 1024 + lane * 16);
+        } else {
+            s_off[u] = (uint32_t)(is_b ? min(n0 + row, N - 1) * ldbs : min(m0 + row, M - 1) * ldas);
+        }
+        s_dst[u] = (is_b ? kBM * 16 : 0) + 1024 * (NW == 4 ? wave : (wave & 3));
+    }
     // fragment and scale reads of this lane
     const int perm = chunk_perm(r);
-    p.a_frag = (wm * 128 + r) * kRowBytes;
-    p.b_frag = kABytes + (wn * 128 + r) * kRowBytes;
-    p.chunk0 = 16 * ((0 + half) ^ perm);
-    p.chunk1 = 16 * ((2 + half) ^ perm);
-    p.sa_lds = kScaleBase + 16 * (wm * 128 + r);
-    p.sb_lds = kScaleBase + 16 * (kBM + wn * 128 + r);
+    const int a_frag = (wm * 128 + r) * kRowBytes;
+    const int b_frag = kABytes + (wn * G::kWaveCols + r) * kRowBytes;
+    const int chunk0 = 16 * ((0 + half) ^ perm);
+    const int chunk1 = 16 * ((2 + half) ^ perm);
+    const int sa_lds = kScaleBase + 16 * (wm * 128 + r);
+    const int sb_lds = kScaleBase + 16 * (kBM + wn * G::kWaveCols + r);
 
     auto dma = [&](int buf, int stage) {
-        uint8_t *dst = lds + buf * kStageBytes + p.dma_row0 * kRowBytes;
-        const uint8_t *asrc = p.aq + (uint32_t)stage * kRowBytes;
-        const uint8_t *bsrc = p.bq + (uint32_t)stage * kRowBytes;
+        uint8_t *dst = lds + buf * kStageBytes + dma_row0 * kRowBytes;
+        const uint32_t step = TILED ? 1024u : (uint32_t)kRowBytes;
+        const uint8_t *asrc = aq + (uint32_t)stage * step;
+        const uint8_t *bsrc = bq + (uint32_t)stage * step;
 #pragma unroll
-        for (int u = 0; u < kDmaPerOperand; ++u)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(asrc + p.a_off[u]),
+        for (int u = 0; u < G::kDmaPerOperand; ++u)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(asrc + a_off[u]),
                                              (lds_void_t *)(dst + u * 1024), 16, 0, 0);
 #pragma unroll
-        for (int u = 0; u < kDmaPerOperand; ++u)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(bsrc + p.b_off[u]),
+        for (int u = 0; u < G::kDmaPerOperand; ++u)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(bsrc + b_off[u]),
                                              (lds_void_t *)(dst + kABytes + u * 1024), 16, 0, 0);
     };
     auto dma_scales = [&](int g) {
-        uint8_t *dst = lds + kScaleBase + (g & 1) * kScaleSlot + 1024 * wave;
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(p.as + 16 * g + p.as_off), (lds_void_t *)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(p.bs + 16 * g + p.bs_off),
-                                         (lds_void_t *)(dst + kBM * 16), 16, 0, 0);
+        uint8_t *dst = lds + kScaleBase + (g & 1) * kScaleSlot;
+#pragma unroll
+        for (int u = 0; u < G::kDmaPerScales; ++u)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(s_src[u] + (TILED ? 1024 : 16) * g + s_off[u]),
+                                             (lds_void_t *)(dst + s_dst[u]), 16, 0, 0);
     };
-    auto read_frags = [&](int buf, int chunk, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+    auto read_frags = [&](int buf, int chunk, u32x4 (&fa)[FI], u32x4 (&fb)[FJ]) {
         const uint8_t *src = lds + buf * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fa[i] = *reinterpret_cast<const u32x4 *>(src + p.a_frag + 32 * i * kRowBytes + chunk);
-            fb[i] = *reinterpret_cast<const u32x4 *>(src + p.b_frag + 32 * i * kRowBytes + chunk);
-        }
+        for (int i = 0; i < FI; ++i)
+            fa[i] = *reinterpret_cast<const u32x4 *>(src + a_frag + 32 * i * kRowBytes + chunk);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            fb[j] = *reinterpret_cast<const u32x4 *>(src + b_frag + 32 * j * kRowBytes + chunk);
     };
     // this lane's scale words of stage s (byte 2 kk + half of word s % 4 of its rows)
-    auto read_scales = [&](int s, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+    auto read_scales = [&](int s, uint32_t (&sa)[FI], uint32_t (&sb)[FJ]) {
         const int off = ((s >> 2) & 1) * kScaleSlot + 4 * (s & 3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = *reinterpret_cast<const uint32_t *>(lds + p.sa_lds + off + 16 * 32 * i);
-            sb[i] = *reinterpret_cast<const uint32_t *>(lds + p.sb_lds + off + 16 * 32 * i);
-        }
+        for (int i = 0; i < FI; ++i)
+            sa[i] = *reinterpret_cast<const uint32_t *>(lds + sa_lds + off + 16 * 32 * i);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            sb[j] = *reinterpret_cast<const uint32_t *>(lds + sb_lds + off + 16 * 32 * j);
     };
 
-    v16f acc[4][4];
+    v16f acc[FI][FJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // 16 MFMAs of one 64-wide sub-step; transposed product: acc[i][j] holds C^T tile (j, i)
-    auto mfma_step = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4], const uint32_t (&sa)[4],
-                         const uint32_t (&sb)[4], auto opsel) {
-        uint32_t xa[4], xb[4];
+    // FI x FJ MFMAs of one 64-wide sub-step; transposed product: acc[i][j] holds C^T tile (j, i)
+    auto mfma_step = [&](const u32x4 (&fa)[FI], const u32x4 (&fb)[FJ], const uint32_t (&sa)[FI],
+                         const uint32_t (&sb)[FJ], auto opsel) {
+        uint32_t xa[FI], xb[FJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xa[i] = sa[i] >> (8 * half);
-            xb[i] = sb[i] >> (8 * half);
-        }
+        for (int i = 0; i < FI; ++i) xa[i] = sa[i] >> (8 * half);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < FJ; ++j) xb[j] = sb[j] >> (8 * half);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
                 mfma_t<decltype(opsel)::value>(acc[i][j], fb[j], fa[i], xb[j], xa[i]);
     };
 
     const int nk = K / kStageK;  // multiple of 4, >= 4
     const int ngroups = nk / 4;
-    u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
-    uint32_t sa0[4], sb0[4], sa1[4], sb1[4];
+    u32x4 fa0[FI], fb0[FJ], fa1[FI], fb1[FJ];
+    uint32_t sa0[FI], sb0[FJ], sa1[FI], sb1[FJ];
 
     // prologue: scales of stages 0-3, then stages 0, 1, 2; wait for the scales and stage 0
     dma_scales(0);
     dma(0, 0);
     dma(1, 1);
     dma(2, 2);
-    wait_vmcnt<2 * kDmaPerStage>();
+    wait_vmcnt<2 * G::kDmaPerStage>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, p.chunk0, fa0, fb0);
+    read_frags(0, chunk0, fa0, fb0);
     read_scales(0, sa0, sb0);
+
+    constexpr int kMfma = FI * FJ;                 // MFMAs per sub-step
+    constexpr int kFragReads = FI + FJ;
 
     // One stage s = 4 g + J (ring buffer J). WAITN = the number of loads issued after those of
     // stage s + 1 at the point of the wait (-1: no next stage); DMA_NEXT: issue stage s + 3;
@@ -304,15 +336,16 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_pipelined(
         constexpr int waitn = decltype(WAITN)::value;
         const int s = 4 * g + j;
         // sub-step 0: read sub-step 1's fragments while these MFMAs run, two after each of the
-        // first four MFMAs
-        read_frags(j, p.chunk1, fa1, fb1);
+        // first MFMAs
+        read_frags(j, chunk1, fa1, fb1);
         mfma_step(fa0, fb0, sa0, sb0, std::integral_constant<int, 0>());
+        constexpr int lead0 = (kFragReads + 1) / 2;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < lead0; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfma - lead0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (waitn >= 0) {
             // stage s + 1 has landed for every wavefront, and every wavefront is done reading
@@ -324,74 +357,74 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_pipelined(
         if constexpr (decltype(DMA_NEXT)::value) dma((j + 3) % 4, s + 3);
         if constexpr (decltype(SCALES_NEXT)::value) dma_scales(g + 1);
         if constexpr (waitn >= 0) {
-            read_frags((j + 1) % 4, p.chunk0, fa0, fb0);
+            read_frags((j + 1) % 4, chunk0, fa0, fb0);
             read_scales(s + 1, sa1, sb1);
         }
         mfma_step(fa1, fb1, sa0, sb0, std::integral_constant<int, 2>());
-        // the DMA first (it has the longest way to go), one or two instructions per MFMA, then
-        // the next stage's fragment and scale reads, early enough to land before sub-step 0
-        constexpr int nvmem = (decltype(DMA_NEXT)::value ? kDmaPerStage : 0) +
-                              (decltype(SCALES_NEXT)::value ? kDmaPerScales : 0);
-        constexpr int nds = waitn >= 0 ? 12 : 0;
-        constexpr int nlead = (nvmem + 1) / 2 + (nds + 1) / 2;
+        // the DMA first (it has the longest way to go), two instructions per MFMA, then the
+        // next stage's fragment and scale reads, early enough to land before sub-step 0
+        constexpr int nvmem = (decltype(DMA_NEXT)::value ? G::kDmaPerStage : 0) +
+                              (decltype(SCALES_NEXT)::value ? G::kDmaPerScales : 0);
+        constexpr int nds = waitn >= 0 ? kFragReads + (kFragReads + 1) / 2 : 0;
+        constexpr int lv = (nvmem + 1) / 2, ld = (nds + 1) / 2;
+        constexpr int lead1 = lv + ld < kMfma ? lv + ld : kMfma;
 #pragma unroll
-        for (int k = 0; k < (nvmem + 1) / 2; ++k) {
+        for (int k = 0; k < lv; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read (DMA)
         }
 #pragma unroll
-        for (int k = 0; k < (nds + 1) / 2; ++k) {
+        for (int k = 0; k < ld; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16 - nlead, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfma - lead1, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa0[i] = sa1[i];
-            sb0[i] = sb1[i];
-        }
+        for (int i = 0; i < FI; ++i) sa0[i] = sa1[i];
+#pragma unroll
+        for (int jj = 0; jj < FJ; ++jj) sb0[jj] = sb1[jj];
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    using W8 = std::integral_constant<int, kDmaPerStage>;
-    using W10 = std::integral_constant<int, kDmaPerStage + kDmaPerScales>;
+    using WS = std::integral_constant<int, G::kDmaPerStage>;
+    using WSS = std::integral_constant<int, G::kDmaPerStage + G::kDmaPerScales>;
     using W0 = std::integral_constant<int, 0>;
     using WNone = std::integral_constant<int, -1>;
     using T = std::true_type;
     using F = std::false_type;
 
     for (int g = 0; g + 1 < ngroups; ++g) {
-        stage(g, I0(), W8(), T(), T());
-        stage(g, I1(), W10(), T(), F());
-        stage(g, I2(), W10(), T(), F());
-        stage(g, I3(), W8(), T(), F());
+        stage(g, I0(), WS(), T(), T());
+        stage(g, I1(), WSS(), T(), F());
+        stage(g, I2(), WSS(), T(), F());
+        stage(g, I3(), WS(), T(), F());
     }
     {
         const int g = ngroups - 1;
-        stage(g, I0(), W8(), T(), F());
-        stage(g, I1(), W8(), F(), F());
+        stage(g, I0(), WS(), T(), F());
+        stage(g, I1(), WS(), F(), F());
         stage(g, I2(), W0(), F(), F());
         stage(g, I3(), WNone(), F(), F());
     }
 
     // epilogue: acc[i][j] register q * 4 + t of lane (r, half) is
-    // C[m0 + 128 wm + 32 i + r][n0 + 128 wn + 32 j + 8 q + 4 half + t]
+    // C[m0 + 128 wm + 32 i + r][n0 + kWaveCols wn + 32 j + 8 q + 4 half + t]
     const bool full_cols = n0 + kBN <= N && (ldc % 4) == 0 && ((uintptr_t)c % 16) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FI; ++i) {
         const int m = m0 + wm * 128 + 32 * i + r;
         if (m >= M) continue;
         float *crow = c + (int64_t)m * ldc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int jj = 0; jj < FJ; ++jj)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * half;
-                const f32x4v v = {alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1],
-                                  alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]};
+                const int n = n0 + wn * G::kWaveCols + 32 * jj + 8 * q + 4 * half;
+                const f32x4v v = {alpha * acc[i][jj][4 * q + 0], alpha * acc[i][jj][4 * q + 1],
+                                  alpha * acc[i][jj][4 * q + 2], alpha * acc[i][jj][4 * q + 3]};
                 if (full_cols) {
                     *reinterpret_cast<f32x4v *>(crow + n) = v;
                 } else {
@@ -422,19 +455,24 @@ hipError_t launch_fill_zero(float *c, int64_t M, int64_t N, int64_t ldc, hipStre
 
 hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                        const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs, int64_t M,
-                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, hipStream_t stream)
+                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, bool tiled, hipStream_t stream)
 {
+    const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * kGemmWaves);
+    if (tiled) {
+        // the caller guarantees K % 512 == 0 and buffers padded to whole 256-row tiles
+        return launch(gemm_mxfp4_pipelined<kGemmWaves, true>, grid, block, 0, stream, aq, lda, as, ldas, bq,
+                      ldb, bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m, tiles_n);
+    }
     const bool scales_aligned = ((uintptr_t)as % 16 == 0) && ((uintptr_t)bs % 16 == 0) &&
                                 ldas % 16 == 0 && ldbs % 16 == 0;
     const bool offsets_fit = (int64_t)(M - 1) * lda + lda <= INT32_MAX && (int64_t)(N - 1) * ldb + ldb <= INT32_MAX;
     if (K % 512 == 0 && K > 0 && scales_aligned && offsets_fit) {
-        const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
-        return launch(gemm_mxfp4_pipelined, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream,
-                      aq, lda, as, ldas, bq, ldb, bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc,
-                      tiles_m, tiles_n);
+        return launch(gemm_mxfp4_pipelined<kGemmWaves, false>, grid, block, 0, stream, aq, lda, as, ldas, bq,
+                      ldb, bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m, tiles_n);
     }
-    const dim3 grid((unsigned)((N + kTileN - 1) / kTileN), (unsigned)((M + kTileM - 1) / kTileM));
-    return launch(gemm_mxfp4_simple, grid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
+    const dim3 sgrid((unsigned)((N + kTileN - 1) / kTileN), (unsigned)((M + kTileM - 1) / kTileM));
+    return launch(gemm_mxfp4_simple, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
                   (int)M, (int)N, (int)K, alpha, c, ldc);
 }
 

@@ -7,19 +7,23 @@
 namespace mx {
 
 // Arguments are validated by the caller; these only pick a kernel and enqueue it.
+// tiled: write the tiled layout (L % 512 == 0; ldq and lds unused), else row-major.
 hipError_t launch_quantize_rows(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
                                 int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
-                                uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
+                                bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream);
 
 hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
                                 int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
-                                uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
+                                bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream);
 
+// tiled: both operands in the tiled layout (K % 512 == 0, rows padded to multiples of 256);
+// otherwise row-major with leading dimensions.
 hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                        const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs, int64_t M,
-                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, hipStream_t stream);
+                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, bool tiled,
+                       hipStream_t stream);
 
 // c[m][n] = 0 for m < M, n < N (a kernel, not a memset, so it is safe inside captured graphs).
 hipError_t launch_fill_zero(float *c, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);

@@ -43,7 +43,18 @@ __device__ __forceinline__ void load8(const char *p, float *v)
     }
 }
 
-template <int H, bool F32, bool SR>
+// Tiled-layout byte offsets (see mxfp4.h): the 16-byte chunk of codes holding elements
+// [32 c, 32 c + 32) of quantized row o, and the scale byte of that block.
+__device__ __forceinline__ int64_t tiled_chunk(uint32_t o, uint32_t c, int64_t L)
+{
+    return ((int64_t)(o / 16) * (L / 128) + c / 4) * 1024 + (o % 16) * 64 + 16 * ((c % 4) ^ ((o % 16) / 4));
+}
+__device__ __forceinline__ int64_t tiled_scale(uint32_t o, uint32_t c, int64_t L)
+{
+    return ((int64_t)(o / 64) * (L / 512) + c / 16) * 1024 + (o % 64) * 16 + (c % 16);
+}
+
+template <int H, bool F32, bool SR, bool TILED>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t groups_per_row, uint32_t total_groups,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
@@ -109,8 +120,14 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
         }
         if (sc == 0xFFu) word = 0u;
         if (live[u]) {
-            __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(q + (int64_t)row[u] * ldq) + grp[u]);
-            if ((lane & 3u) == 0u) scales[(int64_t)row[u] * lds + grp[u] / 4] = (uint8_t)sc;
+            if constexpr (TILED) {
+                const int64_t at = tiled_chunk(row[u], grp[u] / 4, L) + 4 * (grp[u] % 4);
+                __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(q + at));
+                if ((lane & 3u) == 0u) scales[tiled_scale(row[u], grp[u] / 4, L)] = (uint8_t)sc;
+            } else {
+                __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(q + (int64_t)row[u] * ldq) + grp[u]);
+                if ((lane & 3u) == 0u) scales[(int64_t)row[u] * lds + grp[u] / 4] = (uint8_t)sc;
+            }
         }
     }
 }
@@ -130,7 +147,7 @@ constexpr int kColsTileRows = 256;
 constexpr int kColsRowBytes = 128;
 constexpr int kColsOutStride = 144;  // 128 bytes of codes + 16 of padding per output row
 
-template <int H, bool F32, bool SR>
+template <int H, bool F32, bool SR, bool TILED>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t rows, uint32_t cols, uint32_t col_tiles,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
@@ -230,13 +247,19 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
         const uint32_t orow = c0 + tc;
         if (orow < cols && blk < nblocks) {
             const u32x4 t = *reinterpret_cast<const u32x4 *>(out + tc * kColsOutStride + blk * 16);
-            __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(q + (int64_t)orow * ldq + (r0 / 32 + blk) * 16));
-            scales[(int64_t)orow * lds + r0 / 32 + blk] = out_scales[tc * 8 + blk];
+            const uint32_t kb = r0 / 32 + blk;  // block index along the quantized axis
+            if constexpr (TILED) {
+                __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(q + tiled_chunk(orow, kb, rows)));
+                scales[tiled_scale(orow, kb, rows)] = out_scales[tc * 8 + blk];
+            } else {
+                __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(q + (int64_t)orow * ldq + kb * 16));
+                scales[(int64_t)orow * lds + kb] = out_scales[tc * 8 + blk];
+            }
         }
     }
 }
 
-template <int H, bool F32, bool SR>
+template <int H, bool F32, bool SR, bool TILED>
 hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                          hipStream_t stream)
@@ -245,11 +268,11 @@ hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx,
     const uint32_t total = (uint32_t)(rows * (cols / 8));
     const uint32_t per_block = kThreads * kRowsUnroll;
     const dim3 grid((total + per_block - 1) / per_block);
-    return launch(quant_rows_kernel<H, F32, SR>, grid, dim3(kThreads), 0, stream, x, ldx, gpr, total, q,
+    return launch(quant_rows_kernel<H, F32, SR, TILED>, grid, dim3(kThreads), 0, stream, x, ldx, gpr, total, q,
                   ldq, scales, lds, (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, cols);
 }
 
-template <int H, bool F32, bool SR>
+template <int H, bool F32, bool SR, bool TILED>
 hipError_t cols_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                          hipStream_t stream)
@@ -257,7 +280,7 @@ hipError_t cols_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx,
     const int64_t tile_cols = kColsRowBytes / (F32 ? 4 : 2);
     const int64_t col_tiles = (cols + tile_cols - 1) / tile_cols;
     const int64_t row_tiles = (rows + kColsTileRows - 1) / kColsTileRows;
-    return launch(quant_cols_kernel<H, F32, SR>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0,
+    return launch(quant_cols_kernel<H, F32, SR, TILED>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0,
                   stream, x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles, q, ldq, scales, lds,
                   (uint32_t)seed, (uint32_t)(seed >> 32), stream_id);
 }
@@ -281,32 +304,38 @@ hipError_t pick(int h, bool f32, bool sr, A... a)
 template <int H, bool F32, bool SR>
 struct RowsSel {
     template <typename... A>
-    static hipError_t run(A... a) { return rows_dispatch<H, F32, SR>(a...); }
+    static hipError_t run(bool tiled, A... a)
+    {
+        return tiled ? rows_dispatch<H, F32, SR, true>(a...) : rows_dispatch<H, F32, SR, false>(a...);
+    }
 };
 
 template <int H, bool F32, bool SR>
 struct ColsSel {
     template <typename... A>
-    static hipError_t run(A... a) { return cols_dispatch<H, F32, SR>(a...); }
+    static hipError_t run(bool tiled, A... a)
+    {
+        return tiled ? cols_dispatch<H, F32, SR, true>(a...) : cols_dispatch<H, F32, SR, false>(a...);
+    }
 };
 
 }  // namespace
 
 hipError_t launch_quantize_rows(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
                                 int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
-                                uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
+                                bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream)
 {
-    return pick<RowsSel>(hadamard, f32, stochastic, x, rows, cols, ldx, seed, stream_id, q, ldq,
+    return pick<RowsSel>(hadamard, f32, stochastic, tiled, x, rows, cols, ldx, seed, stream_id, q, ldq,
                          scales, lds, stream);
 }
 
 hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
                                 int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
-                                uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
+                                bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream)
 {
-    return pick<ColsSel>(hadamard, f32, stochastic, x, rows, cols, ldx, seed, stream_id, q, ldq,
+    return pick<ColsSel>(hadamard, f32, stochastic, tiled, x, rows, cols, ldx, seed, stream_id, q, ldq,
                          scales, lds, stream);
 }
 

@@ -100,3 +100,28 @@ def down_wgrad(seed=0, m=8192, n=4096, k=14336):
     dy = grads(rng, m, n)
     x = bf16_bits(normal(rng, (m, k)))
     return dy, x
+
+
+# The projections of one decoder layer grouped by the activation they read: q, k, v share the
+# attention input, gate and up share the MLP input.
+LLAMA31_8B_INPUT_OF = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "o_in",
+                       "gate": "mlp_in", "up": "mlp_in", "down": "down_in"}
+
+
+def llama_layer_inputs(seed=0, tokens=8192):
+    """Inputs of every linear projection of one Llama-3.1-8B decoder layer at `tokens` tokens.
+
+    Draw order: the activations attn_in, o_in, mlp_in (each N(0,1) with outlier channels) and
+    down_in (N(0,1)); then per projection in LLAMA31_8B_PROJECTIONS order its W ~ N(0, 0.02^2)
+    and its dY ~ 1e-3 Student-t(3). Returns (acts: name -> X[tokens, K] bits,
+    per_proj: name -> (W[N, K] bits, dY[tokens, N] bits)).
+    """
+    rng = np.random.default_rng(seed)
+    acts = {}
+    for name, k in (("attn_in", 4096), ("o_in", 4096), ("mlp_in", 4096)):
+        acts[name] = activations(rng, tokens, k, outliers=True)
+    acts["down_in"] = activations(rng, tokens, 14336, outliers=False)
+    per_proj = {}
+    for name, (k, n) in LLAMA31_8B_PROJECTIONS.items():
+        per_proj[name] = (weights(rng, n, k), grads(rng, tokens, n))
+    return acts, per_proj

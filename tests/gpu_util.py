@@ -44,3 +44,44 @@ def assert_gemm_close(got, ref, basis, rel=1e-5, what=""):
         raise AssertionError("%s: %d outputs outside tolerance; worst err %.3e vs bound %.3e (ref %.6e)"
                              % (what, int(bad.sum()), err[i], bound[i], ref[ok][i]))
     return float((err / np.maximum(basis[ok], 1e-300)).max()) if err.size else 0.0
+
+
+# ------------------------------------------------------------------ tiled operand layout --
+# The byte permutation include/mxfp4.h defines for MXFP4_LAYOUT_TILED (rows padded to 256):
+# the 16-byte chunk of codes holding block c of row o starts at
+#   ((o / 16) * (L / 128) + c / 4) * 1024 + (o % 16) * 64 + 16 * ((c % 4) ^ ((o % 16) / 4)),
+# and the scale of block c of row o is byte ((o / 64) * (L / 512) + c / 16) * 1024 + (o % 64) * 16
+# + (c % 16).
+
+def _chunk_offsets(R, L):
+    o = np.arange(R)[:, None]
+    c = np.arange(L // 32)[None, :]
+    return ((o // 16) * (L // 128) + c // 4) * 1024 + (o % 16) * 64 + 16 * ((c % 4) ^ ((o % 16) // 4))
+
+
+def _scale_offsets(R, L):
+    o = np.arange(R)[:, None]
+    c = np.arange(L // 32)[None, :]
+    return ((o // 64) * (L // 512) + c // 16) * 1024 + (o % 64) * 16 + (c % 16)
+
+
+def untile(q_flat, s_flat, outer, L):
+    """Row-major (codes [outer, L/2], scales [outer, L/32]) from tiled buffers."""
+    R = (outer + 255) // 256 * 256
+    qb = np.asarray(q_flat, dtype=np.uint8).reshape(-1)
+    sb = np.asarray(s_flat, dtype=np.uint8).reshape(-1)
+    off = _chunk_offsets(R, L)[:outer]
+    q = qb[off[..., None] + np.arange(16)].reshape(outer, L // 2)
+    s = sb[_scale_offsets(R, L)[:outer]]
+    return q, s
+
+
+def tile(q, s, outer, L):
+    """Tiled buffers (flat uint8, rows padded to 256 with zeros) from row-major codes and scales."""
+    R = (outer + 255) // 256 * 256
+    qt = np.zeros(R * L // 2, dtype=np.uint8)
+    st = np.zeros(R * L // 32, dtype=np.uint8)
+    off = _chunk_offsets(R, L)[:outer]
+    qt[off[..., None] + np.arange(16)] = np.asarray(q, dtype=np.uint8).reshape(outer, L // 32, 16)
+    st[_scale_offsets(R, L)[:outer]] = np.asarray(s, dtype=np.uint8)
+    return qt, st

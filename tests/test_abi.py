@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
                      "mxfp4_linear_wgrad", "mxfp4_linear_workspace_bytes", "mxfp4_status_string",
                      "mxfp4_abi_version"):
         assert expected in names
+    assert "mxfp4_tiled_sizes" in names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 1
+    assert L.mxfp4_abi_version() == 2
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -56,8 +57,8 @@ def test_workspace_bytes(L):
 
 
 def _q(L, x=1 << 12, dtype=0, rows=64, cols=64, ldx=64, axis=1, h=16, rnd=0, q=1 << 12, ldq=32,
-       s=1 << 12, lds=2):
-    return L.mxfp4_quantize(x, dtype, rows, cols, ldx, axis, h, rnd, 0, 0, q, ldq, s, lds, None)
+       s=1 << 12, lds=2, layout=0):
+    return L.mxfp4_quantize(x, dtype, rows, cols, ldx, axis, h, rnd, 0, 0, layout, q, ldq, s, lds, None)
 
 
 def test_quantize_argument_errors(L):
@@ -75,11 +76,15 @@ def test_quantize_argument_errors(L):
     assert _q(L, ldx=68) == 4                               # row stride not a multiple of 16 bytes
     assert _q(L, ldq=40) == 4
     assert _q(L, rows=0) == 0 and _q(L, rows=0, x=None) == 0  # empty: nothing to do
+    assert _q(L, layout=2) == 3                             # layout enum
+    assert _q(L, layout=1) == 2                             # tiled needs L % 512 == 0
+    assert _q(L, layout=1, cols=512, ldx=512, s=(1 << 12) + 1) == 4   # tiled scales 16-byte aligned
+    assert _q(L, layout=1, rows=512, cols=64, axis=0, ldq=0, lds=0, q=None) == 1
 
 
 def test_gemm_argument_errors(L):
-    def g(aq=1 << 12, lda=32, bq=1 << 12, ldb=32, M=8, N=8, K=64, c=1 << 12, ldc=8):
-        return L.mxfp4_gemm(aq, lda, 1 << 12, 2, bq, ldb, 1 << 12, 2, M, N, K, 1.0, c, ldc, None)
+    def g(aq=1 << 12, lda=32, bq=1 << 12, ldb=32, M=8, N=8, K=64, c=1 << 12, ldc=8, layout=0, bs=1 << 12):
+        return L.mxfp4_gemm(aq, lda, 1 << 12, 2, bq, ldb, bs, 2, M, N, K, 1.0, c, ldc, layout, None)
     assert g(K=48) == 2
     assert g(M=-2) == 2
     assert g(lda=16) == 3
@@ -88,6 +93,10 @@ def test_gemm_argument_errors(L):
     assert g(aq=None) == 1
     assert g(aq=(1 << 12) + 8) == 4
     assert g(M=0) == 0 and g(N=0, c=None) == 0
+    assert g(layout=3) == 3
+    assert g(layout=1) == 2                                # tiled: K % 512
+    assert g(layout=1, K=512, bs=(1 << 12) + 4) == 4       # tiled scales 16-byte aligned
+    assert g(layout=1, K=1 << 30, M=1 << 14) == 2          # 32-bit tiled offsets
 
 
 def test_linear_argument_errors(L):
@@ -109,3 +118,23 @@ def test_linear_argument_errors(L):
     assert L.mxfp4_linear_wgrad(1 << 12, 1 << 12, 40, 64, 64, ctypes.byref(cfg), 1 << 12, 1 << 30,
                                 1 << 12, None) == 2
     assert f(1 << 12, 1 << 12, 0, 64, 64, ctypes.byref(cfg), None, 0, None, None) == 0
+
+
+def test_tiled_sizes(L):
+    import mxfp4_block_scaled_h16_amd as mx
+    assert mx.tiled_sizes(8192, 4096) == (8192 * 2048, 8192 * 128)
+    assert mx.tiled_sizes(1000, 512) == (1024 * 256, 1024 * 16)      # rows padded to 256
+    assert mx.tiled_sizes(0, 512) == (0, 0)
+    with pytest.raises(mx.Mxfp4Error):
+        mx.tiled_sizes(64, 96)
+
+
+def test_linear_workspace_uses_tiled_padding(L):
+    import mxfp4_block_scaled_h16_amd as mx
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    # Fprop with K = 4096 (tiled): X rows and W rows padded to 256
+    M, K, N = 1000, 4096, 300
+    want = r(r(M) * K // 2) + r(r(M) * K // 32) + r(r(N) * K // 2) + r(r(N) * K // 32)
+    assert mx.workspace_bytes(mx.FPROP, M, K, N) == want
+    # contraction 96 (not a multiple of 512): row-major, no padding
+    assert mx.workspace_bytes(mx.FPROP, 64, 96, 32) == r(64 * 48) + r(64 * 3) + r(32 * 48) + r(32 * 3)

@@ -158,3 +158,20 @@ def test_qkv_fprop_full_size_sampled():
     ns = np.concatenate([rng.integers(0, N, 4000), [0, 0, N - 1, N - 1]])
     ref, basis = oracle.gemm_sampled(*xa, *wb, ms, ns, alpha=1 / 16)
     assert_gemm_close(y[ms, ns], ref, basis, TOL, "qkv fprop sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 520, 1024), (1000, 256, 2048), (512, 768, 4096)])
+def test_gemm_tiled_layout(M, N, K):
+    """The same products from operands in the tiled layout (rows padded to 256)."""
+    from tests.gpu_util import tile
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(M + 3 * N + K)
+    aq, as_ = random_operand(rng, M, K)
+    bq, bs = random_operand(rng, N, K)
+    ra, rb = -(-M // 256) * 256, -(-N // 256) * 256
+    at, ats = (t.reshape(ra, -1) for t in tile(aq, as_, M, K))
+    bt, bts = (t.reshape(rb, -1) for t in tile(bq, bs, N, K))
+    announce("gemm tiled", M, N, K)
+    c = host(mx.gemm(_dev_u8(at), _dev_u8(ats), _dev_u8(bt), _dev_u8(bts), alpha=0.125, layout="tiled", m=M, n=N))
+    ref, basis = oracle.gemm(aq, as_, bq, bs, alpha=0.125, with_abs=True)
+    assert_gemm_close(c, ref, basis, TOL, "tiled gemm %dx%dx%d" % (M, N, K))

@@ -119,3 +119,26 @@ def test_full_size_activations_bit_exact(axis):
     x, w, dy = inputs.linear_inputs(8192, 4096, 6144, seed=0)
     check(x, axis, 16, 0, what="QKV X 8192x4096")
     check(dy, 1 - axis, 16, 1, seed=11, stream_id=0, what="QKV dY 8192x6144 SR")
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("h,rounding", [(16, 0), (32, 0), (16, 1), (0, 1)])
+def test_tiled_layout_bit_exact(axis, h, rounding):
+    """The tiled layout holds exactly the row-major codes and scales, permuted as documented;
+    ragged outer sizes leave the padding rows untouched."""
+    from tests.gpu_util import untile
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(40 + axis + h + rounding)
+    for outer, L in ((300, 512), (256, 1024), (77, 2048)):
+        shape = (outer, L) if axis == 1 else (L, outer)
+        x = inputs.bf16_bits(rng.standard_normal(shape).astype(np.float32) * 2)
+        announce("quantize tiled", shape, "axis", axis, "h", h, "rnd", rounding)
+        ld = -(-shape[1] // 8) * 8          # 16-byte row stride for bf16
+        padded = np.zeros((shape[0], ld), dtype=np.uint16)
+        padded[:, :shape[1]] = x
+        dev = bf16_dev(padded)[:, :shape[1]]
+        q, s = mx.quantize(dev, axis=axis, hadamard=h, rounding=rounding, seed=9, stream_id=1, layout="tiled")
+        qh, sh = untile(host(q), host(s), outer, L)
+        rq, rs = oracle.quantize(x, axis=axis, hadamard=h, rounding=rounding, seed=9, stream=1)
+        assert np.array_equal(sh, rs), "tiled scales differ"
+        assert np.array_equal(qh, rq), "tiled codes differ"
