@@ -169,6 +169,32 @@ class Plan:
         return calls
 
 
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed counter summary, if it was taken on the QKV
+    step with the GEMM source as it is now (otherwise None)."""
+    import hashlib
+    if workload != "qkv":
+        return None
+    path = os.path.join(ROOT, "profiles", "gemm_mxfp4_qkv_step_hbm_bytes.txt")
+    src = os.path.join(ROOT, "mxfp4_block_scaled_h16_amd", "csrc", "gemm.hip")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    if vals.get("gemm_source_digest") != digest:
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(plan, h):
     """The oracle, untuned, on a bounded sample of the same step, projected to the whole step."""
     import numpy as np
@@ -286,7 +312,8 @@ def main():
     n_gemm = sum(1 for _, kind, _, _ in plan.op_list if kind == "gemm")
     achieved = gemm_flops / gemm_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MXFP4_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MXFP4_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / MXFP4_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(args.workload),
                 "kernel": "gemm_mxfp4_pipelined (%d launches per step; achieved = GEMM FLOPs / GEMM time)" % n_gemm,
                 "algorithmic_per_launch": "2*M*N*K = %.1f GFLOP average" % (gemm_flops / n_gemm / 1e9)}
     quantizer = {"gbs": round(q_bytes / q_s / 1e9, 1), "frac_of_hbm": round(q_bytes / q_s / 1e9 / HBM_PEAK_GBS, 4),
