@@ -124,6 +124,15 @@ class Plan:
             if "W" in passes:
                 qbuf((name, "dy_cols"), N, M)
                 self.out[(name, "W")] = f32(N, K)
+        # split-K workspaces of the products with few output tiles (allocated once, outside timing)
+        self.ws = {}
+        for key, c in self.out.items():
+            kc = {"F": None, "D": None, "W": None}[key[1]]
+            name = key[0]
+            K, N = next((k, n) for nm, k, n in projs if nm == name)
+            kc = K if key[1] == "F" else (N if key[1] == "D" else M)
+            need = mx.gemm_workspace_bytes(c.shape[0], c.shape[1], kc)
+            self.ws[key] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         self._build(inp)
 
     def _build(self, inp):
@@ -164,8 +173,8 @@ class Plan:
                              mx.quantize(t, axis, h, rnd, seed, stream, q, s, layout=lay))
             else:
                 qa, qb, out = spec
-                calls.append(lambda qa=self.q[qa], qb=self.q[qb], c=self.out[out], lay=self.layout[qa]:
-                             mx.gemm(qa[0], qa[1], qb[0], qb[1], alpha, c, layout=lay))
+                calls.append(lambda qa=self.q[qa], qb=self.q[qb], c=self.out[out], lay=self.layout[qa], ws=self.ws[out]:
+                             mx.gemm(qa[0], qa[1], qb[0], qb[1], alpha, c, layout=lay, workspace=ws))
         return calls
 
 

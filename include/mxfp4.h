@@ -129,11 +129,19 @@ mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
  * lda, ldb >= K/2 and multiples of 16, ldas, ldbs >= K/32, aq, bq 16-byte aligned. Tiled layout
  * (both operands, as mxfp4_quantize writes it with L = K): K % 512 == 0, all four operand
  * pointers 16-byte aligned, the leading dimensions unused.
+ * workspace (optional, device, 16-byte aligned, ws_bytes >= mxfp4_gemm_workspace_bytes()): lets a
+ * product with few output tiles split its contraction into FP32 partials that a second kernel
+ * adds in a fixed order (deterministic); with workspace == NULL or too small it runs unsplit.
+ * The workspace is in use until the enqueued work finishes.
  */
 mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
                           int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,
-                          mxfp4_layout_t layout, void *stream);
+                          mxfp4_layout_t layout, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes that let mxfp4_gemm split the contraction of an M x N x K product (0 when the
+ * product is not split; also 0 for invalid sizes). */
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Per-operand configuration of one linear-layer GEMM. */
 typedef struct {
@@ -146,7 +154,8 @@ typedef struct {
 
 /*
  * Workspace (device bytes) the linear calls need for the two quantized operands of `pass` at
- * X[M][K], W[N][K], dY[M][N]. Returns 0 for invalid sizes.
+ * X[M][K], W[N][K], dY[M][N] (tiled when the contraction is a multiple of 512), plus the split-K
+ * partials of the product when it is split. Returns 0 for invalid sizes.
  */
 size_t mxfp4_linear_workspace_bytes(mxfp4_pass_t pass, int64_t M, int64_t K, int64_t N);
 

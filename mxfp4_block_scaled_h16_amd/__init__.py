@@ -16,7 +16,7 @@ import torch  # imported first: the library binds to the HIP runtime torch has l
 __all__ = [
     "Mxfp4Error", "quantize", "gemm", "linear_fprop", "linear_dgrad", "linear_wgrad",
     "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD", "ROWS", "TILED",
-    "tiled_sizes",
+    "tiled_sizes", "gemm_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,8 +58,10 @@ def lib():
     L.mxfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, u64, u32, ci, vp, i64, vp, i64, vp]
     L.mxfp4_quantize.restype = ci
     L.mxfp4_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64,
-                             ci, vp]
+                             ci, vp, ctypes.c_size_t, vp]
     L.mxfp4_gemm.restype = ci
+    L.mxfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    L.mxfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
     L.mxfp4_tiled_sizes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     L.mxfp4_tiled_sizes.restype = ci
     L.mxfp4_linear_workspace_bytes.argtypes = [ci, i64, i64, i64]
@@ -154,10 +156,17 @@ def quantize(x, axis=1, hadamard=16, rounding="rne", seed=0, stream_id=0, q=None
     return q, scales
 
 
-def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None, layout="rows", m=None, n=None):
+def gemm_workspace_bytes(M, N, K) -> int:
+    return int(lib().mxfp4_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None, layout="rows", m=None, n=None,
+         workspace=None):
     """c[m][n] = alpha * sum_k deq(A)[m][k] deq(B)[n][k] (FP32 [M, N]).
 
-    Tiled operands are padded to 256 rows, so M and N come from `out`, or `m` and `n`."""
+    Tiled operands are padded to 256 rows, so M and N come from `out`, or `m` and `n`. A device
+    workspace of gemm_workspace_bytes(M, N, K) bytes lets few-tile products split K; "auto"
+    allocates it."""
     lay = _layout(layout)
     for t, nm in ((aq, "aq"), (as_, "as"), (bq, "bq"), (bs, "bs")):
         _require_cuda(t, nm)
@@ -169,9 +178,14 @@ def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None, layout="rows", m=Non
     N = N if n is None else int(n)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=aq.device)
+    if isinstance(workspace, str) and workspace == "auto":
+        need = gemm_workspace_bytes(M, N, K)
+        workspace = torch.empty(need, dtype=torch.uint8, device=aq.device) if need else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().mxfp4_gemm(aq.data_ptr(), aq.stride(0), as_.data_ptr(), as_.stride(0), bq.data_ptr(),
                           bq.stride(0), bs.data_ptr(), bs.stride(0), M, N, K, float(alpha),
-                          out.data_ptr(), out.stride(0), lay, _stream(stream))
+                          out.data_ptr(), out.stride(0), lay, ws_ptr, ws_len, _stream(stream))
     _check(st, "mxfp4_gemm")
     return out
 

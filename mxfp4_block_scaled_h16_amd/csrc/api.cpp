@@ -106,6 +106,12 @@ size_t layout_bytes(const OperandSpace &a, const OperandSpace &b)
     return round256(a.codes()) + round256(a.scales()) + round256(b.codes()) + round256(b.scales());
 }
 
+// bytes of the operand part plus the split-K partials of the (out_rows x out_cols x kc) product
+size_t linear_bytes(const OperandSpace &a, const OperandSpace &b, int64_t out_rows, int64_t out_cols, int64_t kc)
+{
+    return layout_bytes(a, b) + round256(mx::gemm_workspace_bytes(out_rows, out_cols, kc));
+}
+
 bool pass_operands(mxfp4_pass_t pass, int64_t M, int64_t K, int64_t N, OperandSpace *a, OperandSpace *b)
 {
     switch (pass) {
@@ -152,7 +158,7 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     if (!sp.a_src || !sp.b_src) return MXFP4_ERR_NULL;
     if (!aligned(sp.a_src, 16) || !aligned(sp.b_src, 16)) return MXFP4_ERR_ALIGN;
     if ((sp.a_cols * 2) % 16 != 0 || (sp.b_cols * 2) % 16 != 0) return MXFP4_ERR_ALIGN;
-    const size_t need = layout_bytes(a, b);
+    const size_t need = linear_bytes(a, b, sp.out_rows, sp.out_cols, sp.kc);
     if (!ws || ws_bytes < need) return MXFP4_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return MXFP4_ERR_ALIGN;
     if (mxfp4_status_t st = check_device()) return st;
@@ -177,7 +183,8 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     if (e == hipSuccess) e = quant(sp.b_src, sp.b_rows, sp.b_cols, sp.b_axis, cfg->rnd_b, 1u, bq, bs, b.L);
     if (e == hipSuccess)
         e = mx::launch_gemm(aq, a.L / 2, as, a.L / 32, bq, b.L / 2, bs, b.L / 32, sp.out_rows,
-                            sp.out_cols, sp.kc, alpha, out, sp.out_cols, tiled, s);
+                            sp.out_cols, sp.kc, alpha, out, sp.out_cols, tiled, p + layout_bytes(a, b),
+                            ws_bytes - layout_bytes(a, b), s);
     return from_hip(e);
 }
 
@@ -208,7 +215,7 @@ mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
 mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
                           int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,
-                          mxfp4_layout_t layout, void *stream)
+                          mxfp4_layout_t layout, void *workspace, size_t ws_bytes, void *stream)
 {
     mxfp4_status_t st = check_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, c, ldc, layout);
     if (st != MXFP4_OK || M == 0 || N == 0) return st;
@@ -218,7 +225,14 @@ mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int
         return from_hip(mx::launch_fill_zero(c, M, N, ldc, (hipStream_t)stream));
     }
     return from_hip(mx::launch_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, alpha, c, ldc,
-                                    layout == MXFP4_LAYOUT_TILED, (hipStream_t)stream));
+                                    layout == MXFP4_LAYOUT_TILED, workspace, ws_bytes,
+                                    (hipStream_t)stream));
+}
+
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+    return mx::gemm_workspace_bytes(M, N, K);
 }
 
 mxfp4_status_t mxfp4_tiled_sizes(int64_t outer, int64_t L, size_t *codes_bytes, size_t *scales_bytes)
@@ -235,7 +249,10 @@ size_t mxfp4_linear_workspace_bytes(mxfp4_pass_t pass, int64_t M, int64_t K, int
     if (M < 0 || K < 0 || N < 0 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
     OperandSpace a, b;
     if (!pass_operands(pass, M, K, N, &a, &b)) return 0;
-    return layout_bytes(a, b);
+    // product shape of the pass: Fprop M x N (K), Dgrad M x K (N), Wgrad N x K (M)
+    if (pass == MXFP4_FPROP) return linear_bytes(a, b, M, N, K);
+    if (pass == MXFP4_DGRAD) return linear_bytes(a, b, M, K, N);
+    return linear_bytes(a, b, N, K, M);
 }
 
 mxfp4_status_t mxfp4_linear_fprop(const void *x_bf16, const void *w_bf16, int64_t M, int64_t K,

@@ -172,7 +172,8 @@ template <int NW, bool TILED>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
-    int M, int N, int K, float alpha, float *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n)
+    int M, int N, int K, float alpha, float *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n,
+    int splits, float *__restrict__ partials)
 {
     using G = Geo<NW>;
     constexpr int FI = G::FI, FJ = G::FJ;
@@ -181,7 +182,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     // tile order: consecutive workgroups are spread over the 8 XCDs; give each XCD a contiguous
     // range of tiles, walked column-panel by column-panel in groups of 8 row panels
     const int total = tiles_m * tiles_n;
-    int t = blockIdx.x;
+    // split-K: workgroup blockIdx.x covers K-split blockIdx.x / total of tile blockIdx.x % total
+    const int split = blockIdx.x / total;
+    int t = blockIdx.x % total;
     if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;
     const int group = 8 * tiles_n;
     const int g0 = (t / group) * 8;
@@ -245,11 +248,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     const int sa_lds = kScaleBase + 16 * (wm * 128 + r);
     const int sb_lds = kScaleBase + 16 * (kBM + wn * G::kWaveCols + r);
 
+    const int stage0 = split * (K / kStageK / splits);  // first stage of this split
     auto dma = [&](int buf, int stage) {
         uint8_t *dst = lds + buf * kStageBytes + dma_row0 * kRowBytes;
         const uint32_t step = TILED ? 1024u : (uint32_t)kRowBytes;
-        const uint8_t *asrc = aq + (uint32_t)stage * step;
-        const uint8_t *bsrc = bq + (uint32_t)stage * step;
+        const uint8_t *asrc = aq + (uint32_t)(stage0 + stage) * step;
+        const uint8_t *bsrc = bq + (uint32_t)(stage0 + stage) * step;
 #pragma unroll
         for (int u = 0; u < G::kDmaPerOperand; ++u)
             __builtin_amdgcn_global_load_lds((gbl_void_t *)(asrc + a_off[u]),
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
         uint8_t *dst = lds + kScaleBase + (g & 1) * kScaleSlot;
 #pragma unroll
         for (int u = 0; u < G::kDmaPerScales; ++u)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(s_src[u] + (TILED ? 1024 : 16) * g + s_off[u]),
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(s_src[u] + (TILED ? 1024 : 16) * (stage0 / 4 + g) + s_off[u]),
                                              (lds_void_t *)(dst + s_dst[u]), 16, 0, 0);
     };
     auto read_frags = [&](int buf, int chunk, u32x4 (&fa)[FI], u32x4 (&fb)[FJ]) {
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
                 mfma_t<decltype(opsel)::value>(acc[i][j], fb[j], fa[i], xb[j], xa[i]);
     };
 
-    const int nk = K / kStageK;  // multiple of 4, >= 4
+    const int nk = K / kStageK / splits;  // stages of this split: a multiple of 4, >= 4
     const int ngroups = nk / 4;
     u32x4 fa0[FI], fb0[FJ], fa1[FI], fb1[FJ];
     uint32_t sa0[FI], sb0[FJ], sa1[FI], sb1[FJ];
@@ -411,7 +415,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     }
 
     // epilogue: acc[i][j] register q * 4 + t of lane (r, half) is
-    // C[m0 + 128 wm + 32 i + r][n0 + kWaveCols wn + 32 j + 8 q + 4 half + t]
+    // C[m0 + 128 wm + 32 i + r][n0 + kWaveCols wn + 32 j + 8 q + 4 half + t]. With split-K the
+    // unscaled partial product goes to partials[split][M][N] instead.
+    if (splits > 1) {
+        c = partials + (int64_t)split * M * N;
+        ldc = N;
+        alpha = 1.0f;
+    }
     const bool full_cols = n0 + kBN <= N && (ldc % 4) == 0 && ((uintptr_t)c % 16) == 0;
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
@@ -443,6 +453,19 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ c, i
     if (i < M * N) c[(i / N) * ldc + (i % N)] = 0.0f;
 }
 
+// c[m][n] = alpha * (p_0[m][n] + p_1[m][n] + ... + p_{S-1}[m][n]), summed in that fixed order
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ p, int splits, int64_t M,
+                                                            int64_t N, float alpha, float *__restrict__ c,
+                                                            int64_t ldc)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= M * N) return;
+    const int64_t mn = M * N;
+    float acc = p[i];
+    for (int s = 1; s < splits; ++s) acc += p[(int64_t)s * mn + i];
+    c[(i / N) * ldc + (i % N)] = alpha * acc;
+}
+
 }  // namespace
 
 hipError_t launch_fill_zero(float *c, int64_t M, int64_t N, int64_t ldc, hipStream_t stream)
@@ -453,27 +476,56 @@ hipError_t launch_fill_zero(float *c, int64_t M, int64_t N, int64_t ldc, hipStre
                   N, ldc);
 }
 
+int gemm_splits(int64_t M, int64_t N, int64_t K)
+{
+    // split the contraction only when the output has at most 32 tiles of 256 x 256 (an eighth of
+    // the compute units): under the board's power cap a few busy CUs clock higher, and at 64
+    // tiles the partials' extra HBM traffic already cancels the gain. Each split keeps at least
+    // 1024 values of K (whole 512-groups).
+    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    if (K % 512 != 0 || tiles > 32) return 1;
+    int s = 1;
+    while (s < 8 && tiles * s * 2 <= 256 && (K / 512) % (s * 2) == 0 && K / (512 * s * 2) >= 2) s *= 2;
+    return s;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int s = gemm_splits(M, N, K);
+    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                        const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs, int64_t M,
-                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, bool tiled, hipStream_t stream)
+                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, bool tiled,
+                       void *workspace, size_t ws_bytes, hipStream_t stream)
 {
     const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * kGemmWaves);
-    if (tiled) {
-        // the caller guarantees K % 512 == 0 and buffers padded to whole 256-row tiles
-        return launch(gemm_mxfp4_pipelined<kGemmWaves, true>, grid, block, 0, stream, aq, lda, as, ldas, bq,
-                      ldb, bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m, tiles_n);
-    }
     const bool scales_aligned = ((uintptr_t)as % 16 == 0) && ((uintptr_t)bs % 16 == 0) &&
                                 ldas % 16 == 0 && ldbs % 16 == 0;
     const bool offsets_fit = (int64_t)(M - 1) * lda + lda <= INT32_MAX && (int64_t)(N - 1) * ldb + ldb <= INT32_MAX;
-    if (K % 512 == 0 && K > 0 && scales_aligned && offsets_fit) {
-        return launch(gemm_mxfp4_pipelined<kGemmWaves, false>, grid, block, 0, stream, aq, lda, as, ldas, bq,
-                      ldb, bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m, tiles_n);
+    // tiled: the caller guarantees K % 512 == 0 and buffers padded to whole 256-row tiles
+    const bool pipelined = tiled || (K % 512 == 0 && K > 0 && scales_aligned && offsets_fit);
+    if (!pipelined) {
+        const dim3 sgrid((unsigned)((N + kTileN - 1) / kTileN), (unsigned)((M + kTileM - 1) / kTileM));
+        return launch(gemm_mxfp4_simple, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
+                      (int)M, (int)N, (int)K, alpha, c, ldc);
     }
-    const dim3 sgrid((unsigned)((N + kTileN - 1) / kTileN), (unsigned)((M + kTileM - 1) / kTileM));
-    return launch(gemm_mxfp4_simple, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
-                  (int)M, (int)N, (int)K, alpha, c, ldc);
+    int splits = gemm_splits(M, N, K);
+    if (splits > 1 && (workspace == nullptr || ws_bytes < gemm_workspace_bytes(M, N, K) ||
+                       (uintptr_t)workspace % 16 != 0))
+        splits = 1;
+    float *partials = splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    const dim3 grid((unsigned)(tiles_m * tiles_n * splits)), block(64 * kGemmWaves);
+    hipError_t e = tiled
+        ? launch(gemm_mxfp4_pipelined<kGemmWaves, true>, grid, block, 0, stream, aq, lda, as, ldas, bq, ldb,
+                 bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m, tiles_n, splits, partials)
+        : launch(gemm_mxfp4_pipelined<kGemmWaves, false>, grid, block, 0, stream, aq, lda, as, ldas, bq, ldb,
+                 bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m, tiles_n, splits, partials);
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t total = M * N;
+    return launch(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                  (const float *)partials, splits, M, N, alpha, c, ldc);
 }
 
 }  // namespace mx

@@ -19,11 +19,15 @@ hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t c
                                 hipStream_t stream);
 
 // tiled: both operands in the tiled layout (K % 512 == 0, rows padded to multiples of 256);
-// otherwise row-major with leading dimensions.
+// otherwise row-major with leading dimensions. A workspace of gemm_workspace_bytes() bytes
+// (16-byte aligned) lets a GEMM with few output tiles split K (gemm_splits() ways) into FP32
+// partials that a second kernel sums in fixed order; without it the GEMM runs unsplit.
 hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                        const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs, int64_t M,
                        int64_t N, int64_t K, float alpha, float *c, int64_t ldc, bool tiled,
-                       hipStream_t stream);
+                       void *workspace, size_t ws_bytes, hipStream_t stream);
+int gemm_splits(int64_t M, int64_t N, int64_t K);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // c[m][n] = 0 for m < M, n < N (a kernel, not a memset, so it is safe inside captured graphs).
 hipError_t launch_fill_zero(float *c, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);

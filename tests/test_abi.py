@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
                      "mxfp4_linear_wgrad", "mxfp4_linear_workspace_bytes", "mxfp4_status_string",
                      "mxfp4_abi_version"):
         assert expected in names
-    assert "mxfp4_tiled_sizes" in names
+    assert "mxfp4_tiled_sizes" in names and "mxfp4_gemm_workspace_bytes" in names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -84,7 +84,7 @@ def test_quantize_argument_errors(L):
 
 def test_gemm_argument_errors(L):
     def g(aq=1 << 12, lda=32, bq=1 << 12, ldb=32, M=8, N=8, K=64, c=1 << 12, ldc=8, layout=0, bs=1 << 12):
-        return L.mxfp4_gemm(aq, lda, 1 << 12, 2, bq, ldb, bs, 2, M, N, K, 1.0, c, ldc, layout, None)
+        return L.mxfp4_gemm(aq, lda, 1 << 12, 2, bq, ldb, bs, 2, M, N, K, 1.0, c, ldc, layout, None, 0, None)
     assert g(K=48) == 2
     assert g(M=-2) == 2
     assert g(lda=16) == 3
@@ -129,12 +129,29 @@ def test_tiled_sizes(L):
         mx.tiled_sizes(64, 96)
 
 
+def test_gemm_split_policy(L):
+    import mxfp4_block_scaled_h16_amd as mx
+    # 512 x 4096 output = 32 tiles of 256 x 256: K = 8192 splits 8 ways (256 workgroups)
+    assert mx.gemm_workspace_bytes(512, 4096, 8192) == 8 * 512 * 4096 * 4
+    assert mx.gemm_workspace_bytes(1024, 4096, 8192) == 0      # 64 tiles: not split
+    assert mx.gemm_workspace_bytes(8192, 6144, 4096) == 0      # 768 tiles: no split
+    assert mx.gemm_workspace_bytes(256, 256, 2048) == 2 * 256 * 256 * 4   # one tile: 2 splits of 1024
+    assert mx.gemm_workspace_bytes(256, 256, 8192) == 8 * 256 * 256 * 4   # at most 8 splits
+    assert mx.gemm_workspace_bytes(256, 256, 1024) == 0         # each split keeps >= 1024 values of K
+    assert mx.gemm_workspace_bytes(256, 256, 512) == 0
+    assert mx.gemm_workspace_bytes(256, 256, 96) == 0          # not a multiple of 512
+    assert mx.gemm_workspace_bytes(-1, 4, 512) == 0
+
+
 def test_linear_workspace_uses_tiled_padding(L):
     import mxfp4_block_scaled_h16_amd as mx
     r = lambda v: (v + 255) // 256 * 256  # noqa: E731
     # Fprop with K = 4096 (tiled): X rows and W rows padded to 256
     M, K, N = 1000, 4096, 300
     want = r(r(M) * K // 2) + r(r(M) * K // 32) + r(r(N) * K // 2) + r(r(N) * K // 32)
+    # 1000 x 300 output = 8 tiles: the product splits K four ways into FP32 partials
+    want += r(mx.gemm_workspace_bytes(M, N, K))
+    assert mx.gemm_workspace_bytes(M, N, K) == 4 * M * N * 4
     assert mx.workspace_bytes(mx.FPROP, M, K, N) == want
     # contraction 96 (not a multiple of 512): row-major, no padding
     assert mx.workspace_bytes(mx.FPROP, 64, 96, 32) == r(64 * 48) + r(64 * 3) + r(32 * 48) + r(32 * 3)

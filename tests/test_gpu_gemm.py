@@ -175,3 +175,28 @@ def test_gemm_tiled_layout(M, N, K):
     c = host(mx.gemm(_dev_u8(at), _dev_u8(ats), _dev_u8(bt), _dev_u8(bts), alpha=0.125, layout="tiled", m=M, n=N))
     ref, basis = oracle.gemm(aq, as_, bq, bs, alpha=0.125, with_abs=True)
     assert_gemm_close(c, ref, basis, TOL, "tiled gemm %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K,layout", [(256, 256, 2048, "rows"), (512, 4096, 8192, "tiled"),
+                                          (300, 520, 4096, "tiled"), (200, 72, 8192, "rows")])
+def test_gemm_split_k_with_workspace(M, N, K, layout):
+    """Products with few output tiles split K into FP32 partials summed in a fixed order: within
+    tolerance of the oracle and bitwise identical run to run."""
+    from tests.gpu_util import tile
+    import mxfp4_block_scaled_h16_amd as mx
+    assert mx.gemm_workspace_bytes(M, N, K) > 0, "shape expected to split"
+    rng = np.random.default_rng(M * 5 + N + K)
+    aq, as_ = random_operand(rng, M, K)
+    bq, bs = random_operand(rng, N, K)
+    if layout == "tiled":
+        ra, rb = -(-M // 256) * 256, -(-N // 256) * 256
+        da = [_dev_u8(t.reshape(ra, -1)) for t in tile(aq, as_, M, K)]
+        db = [_dev_u8(t.reshape(rb, -1)) for t in tile(bq, bs, N, K)]
+    else:
+        da, db = [_dev_u8(aq), _dev_u8(as_)], [_dev_u8(bq), _dev_u8(bs)]
+    announce("gemm split-k", M, N, K, layout)
+    c1 = host(mx.gemm(*da, *db, alpha=0.25, layout=layout, m=M, n=N, workspace="auto"))
+    c2 = host(mx.gemm(*da, *db, alpha=0.25, layout=layout, m=M, n=N, workspace="auto"))
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32)), "split-K result not deterministic"
+    ref, basis = oracle.gemm(aq, as_, bq, bs, alpha=0.25, with_abs=True)
+    assert_gemm_close(c1, ref, basis, TOL, "split-k gemm %dx%dx%d" % (M, N, K))
