@@ -30,6 +30,7 @@ METRIC = "MXFP4 GEMM TFLOP/s incl. H16+quant (Fprop/Dgrad/Wgrad) + quantizer GB/
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4/FP6 matrix peak, published
 QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0   # bf16 in, 4-bit code out, one E8M0 byte per 32
+DUAL_BYTES_PER_ELEM = 2.0 + 2 * (0.5 + 1.0 / 32.0)  # one read, both quantizations written
 
 # name: (description, [(projection, K, N)], input of each projection, passes, tokens)
 LLAMA_PROJ = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
@@ -53,6 +54,8 @@ def parse_args():
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="qkv")
     p.add_argument("--hadamard", type=int, default=16, choices=[0, 16, 32])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--separate-quant", action="store_true",
+                   help="one quantizer launch per axis instead of one dual launch per tensor")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -61,11 +64,12 @@ def parse_args():
 class Plan:
     """Buffers and the ordered launch list of one step (quantize and GEMM launches)."""
 
-    def __init__(self, mx, torch, workload, h, sets):
+    def __init__(self, mx, torch, workload, h, sets, dual=True):
         import numpy as np
         from synth import inputs
         desc, projs, passes, M = WORKLOADS[workload]
         self.mx, self.torch, self.h, self.passes, self.M = mx, torch, h, passes, M
+        self.dual = dual
         self.alpha = 1.0 / h if h else 1.0
         dev = "cuda"
         to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
@@ -136,29 +140,66 @@ class Plan:
         self._build(inp)
 
     def _build(self, inp):
-        """Launch order: per activation its shared quantizations, then per projection its passes."""
-        M, h = self.M, self.h
-        ops = []
-        done = set()
+        """Launch order: per projection its passes, each preceded by the quantizations it needs
+        that have not run yet. A tensor quantized along both axes in the step (X, W, dY when the
+        passes need both) gets one dual launch, placed where its first output is needed, unless
+        the plan was built with separate quantizer launches."""
+        M = self.M
+        quants = []   # (label, src, key, axis, rounding, seed, stream, dst, elems), in first-use order
+        seen = set()
+
+        def need(label, src, key, axis, rnd, seed, stream, dst, elems):
+            if dst not in seen:
+                seen.add(dst)
+                quants.append((label, src, key, axis, rnd, seed, stream, dst, elems))
+            return dst
+        steps = []    # ("gemm", label, qa, qb, out, flops) with the quantizations listed before it
         for name, K, N in self.projs:
             a = inp[name]
-            if "F" in self.passes and (a, "rows") not in done:
-                ops.append(("quant_rows %s" % a, "quant", ("act", a, 1, "rne", 0, 0, (a, "rows")), M * K))
-                done.add((a, "rows"))
-            if "W" in self.passes and (a, "cols") not in done:
-                ops.append(("quant_cols %s sr" % a, "quant", ("act", a, 0, "sr", 0x5EED, 1, (a, "cols")), M * K))
-                done.add((a, "cols"))
             if "F" in self.passes:
-                ops.append(("quant_rows W_%s" % name, "quant", ("w", name, 1, "rne", 0, 1, (name, "w_rows")), N * K))
-                ops.append(("gemm Fprop %s" % name, "gemm", ((a, "rows"), (name, "w_rows"), (name, "F")), 2.0 * M * N * K))
+                qa = need("x", "act", a, 1, "rne", 0, 0, (a, "rows"), M * K)
+                qb = need("W", "w", name, 1, "rne", 0, 1, (name, "w_rows"), N * K)
+                steps.append(("gemm Fprop %s" % name, qa, qb, (name, "F"), 2.0 * M * N * K))
             if "D" in self.passes:
-                ops.append(("quant_rows dY_%s" % name, "quant", ("dy", name, 1, "rne", 0, 0, (name, "dy_rows")), M * N))
-                ops.append(("quant_cols W_%s" % name, "quant", ("w", name, 0, "rne", 0, 1, (name, "w_cols")), N * K))
-                ops.append(("gemm Dgrad %s" % name, "gemm", ((name, "dy_rows"), (name, "w_cols"), (name, "D")), 2.0 * M * N * K))
+                qa = need("dY", "dy", name, 1, "rne", 0, 0, (name, "dy_rows"), M * N)
+                qb = need("W", "w", name, 0, "rne", 0, 1, (name, "w_cols"), N * K)
+                steps.append(("gemm Dgrad %s" % name, qa, qb, (name, "D"), 2.0 * M * N * K))
             if "W" in self.passes:
-                ops.append(("quant_cols dY_%s sr" % name, "quant", ("dy", name, 0, "sr", 0x5EED, 0, (name, "dy_cols")), M * N))
-                ops.append(("gemm Wgrad %s" % name, "gemm", ((name, "dy_cols"), (a, "cols"), (name, "W")), 2.0 * M * N * K))
+                qa = need("dY", "dy", name, 0, "sr", 0x5EED, 0, (name, "dy_cols"), M * N)
+                qb = need("x", "act", a, 0, "sr", 0x5EED, 1, (a, "cols"), M * K)
+                steps.append(("gemm Wgrad %s" % name, qa, qb, (name, "W"), 2.0 * M * N * K))
+        by_dst = {q[7]: q for q in quants}
+        by_src = {}
+        for q in quants:
+            by_src.setdefault((q[1], q[2]), []).append(q)
+        ops, done = [], set()
+
+        def emit(dst):
+            if dst in done:
+                return
+            q = by_dst[dst]
+            both = by_src[(q[1], q[2])]
+            if self.dual and len(both) == 2:
+                q1 = next(t for t in both if t[3] == 1)
+                q0 = next(t for t in both if t[3] == 0)
+                tensor = q[2] if q[1] == "act" else "%s_%s" % (q[0], q[2])
+                ops.append(("quant_dual %s" % tensor, "dual", (q1, q0), q[8]))
+                done.add(q1[7])
+                done.add(q0[7])
+            else:
+                tensor = q[2] if q[1] == "act" else "%s_%s" % (q[0], q[2])
+                ops.append(("quant_%s %s%s" % ("rows" if q[3] == 1 else "cols", tensor,
+                                                 " sr" if q[4] == "sr" else ""), "quant", q, q[8]))
+                done.add(dst)
+        for label, qa, qb, out, flops in steps:
+            emit(qa)
+            emit(qb)
+            ops.append((label, "gemm", (qa, qb, out), flops))
         self.op_list = ops
+
+    def _tensor(self, d_acts, d_proj, q):
+        src, key = q[1], q[2]
+        return d_acts[key] if src == "act" else d_proj[key][0 if src == "w" else 1]
 
     def launches(self, step_index):
         mx, h, alpha = self.mx, self.h, self.alpha
@@ -166,11 +207,19 @@ class Plan:
         calls = []
         for label, kind, spec, work in self.op_list:
             if kind == "quant":
-                src, key, axis, rnd, seed, stream, dst = spec
-                t = d_acts[key] if src == "act" else d_proj[key][0 if src == "w" else 1]
+                t = self._tensor(d_acts, d_proj, spec)
+                _, _, _, axis, rnd, seed, stream, dst, _ = spec
                 q, s = self.q[dst]
                 calls.append(lambda t=t, axis=axis, rnd=rnd, seed=seed, stream=stream, q=q, s=s, lay=self.layout[dst]:
                              mx.quantize(t, axis, h, rnd, seed, stream, q, s, layout=lay))
+            elif kind == "dual":
+                q1, q0 = spec
+                t = self._tensor(d_acts, d_proj, q1)
+                o1 = dict(rounding=q1[4], seed=q1[5], stream_id=q1[6], layout=self.layout[q1[7]],
+                          q=self.q[q1[7]][0], scales=self.q[q1[7]][1])
+                o0 = dict(rounding=q0[4], seed=q0[5], stream_id=q0[6], layout=self.layout[q0[7]],
+                          q=self.q[q0[7]][0], scales=self.q[q0[7]][1])
+                calls.append(lambda t=t, o1=o1, o0=o0: mx.quantize_dual(t, h, o1, o0))
             else:
                 qa, qb, out = spec
                 calls.append(lambda qa=self.q[qa], qb=self.q[qb], c=self.out[out], lay=self.layout[qa], ws=self.ws[out]:
@@ -230,11 +279,10 @@ def cpu_baseline(plan, h):
     rate_cols = slw.size / (time.perf_counter() - t0)
     t_quant = 0.0
     for label, kind, spec, work in plan.op_list:
-        if kind != "quant":
-            continue
-        axis, rnd = spec[2], spec[3]
-        rate = rate_rows if axis == 1 else (rate_cols_sr if rnd == "sr" else rate_cols)
-        t_quant += work / rate
+        for q in (spec if kind == "dual" else (spec,) if kind == "quant" else ()):
+            axis, rnd = q[3], q[4]
+            rate = rate_rows if axis == 1 else (rate_cols_sr if rnd == "sr" else rate_cols)
+            t_quant += work / rate
     # GEMM rate: 8 output rows of the first projection's Fprop-shaped product
     qa = oracle.quantize(np.ascontiguousarray(any_act[:8]), 1, h, oracle.RNE)
     qb = oracle.quantize(w0, 1, h, oracle.RNE, stream=1) if w0.shape[1] == any_act.shape[1] else None
@@ -273,7 +321,7 @@ def main():
         in_bytes += 2 * (N * K + M * N)
     in_bytes += 2 * M * sum(K for name, K, N in projs)
     sets = max(1, min(8, -(-(1 << 30) // in_bytes)))
-    plan = Plan(mx, torch, args.workload, h, sets)
+    plan = Plan(mx, torch, args.workload, h, sets, dual=not args.separate_quant)
     torch.cuda.synchronize()
 
     for s in range(args.warmup):
@@ -313,8 +361,9 @@ def main():
             gemm_flops += work
             gemm_s += float(t) * 1e-3
         else:
-            entry["gbs"] = round(work * QUANT_BYTES_PER_ELEM / (t * 1e-3) / 1e9, 1)
-            q_bytes += work * QUANT_BYTES_PER_ELEM
+            nbytes = work * (DUAL_BYTES_PER_ELEM if kind == "dual" else QUANT_BYTES_PER_ELEM)
+            entry["gbs"] = round(nbytes / (t * 1e-3) / 1e9, 1)
+            q_bytes += nbytes
             q_s += float(t) * 1e-3
         kernels[label] = entry
 
@@ -326,7 +375,8 @@ def main():
                 "kernel": "gemm_mxfp4_pipelined (%d launches per step; achieved = GEMM FLOPs / GEMM time)" % n_gemm,
                 "algorithmic_per_launch": "2*M*N*K = %.1f GFLOP average" % (gemm_flops / n_gemm / 1e9)}
     quantizer = {"gbs": round(q_bytes / q_s / 1e9, 1), "frac_of_hbm": round(q_bytes / q_s / 1e9 / HBM_PEAK_GBS, 4),
-                 "bytes_per_elem": QUANT_BYTES_PER_ELEM, "us_per_step": round(q_s * 1e6, 1)}
+                 "bytes_per_elem": {"single": QUANT_BYTES_PER_ELEM, "dual": DUAL_BYTES_PER_ELEM},
+                 "launches": "dual" if plan.dual else "separate", "us_per_step": round(q_s * 1e6, 1)}
 
     if args.copy_calibration:
         buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 2
+#define MXFP4_ABI_VERSION 3
 
 typedef enum {
     MXFP4_OK = 0,
@@ -116,6 +116,35 @@ mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
                               int64_t ldx, int axis, int hadamard, mxfp4_rounding_t rounding,
                               uint64_t seed, uint32_t stream_id, mxfp4_layout_t layout, uint8_t *q,
                               int64_t ldq, uint8_t *scales, int64_t lds, void *stream);
+
+/* One output of mxfp4_quantize_dual: what mxfp4_quantize takes for that axis. */
+typedef struct {
+    mxfp4_rounding_t rounding;
+    uint64_t seed;
+    uint32_t stream_id;
+    mxfp4_layout_t layout;
+    uint8_t *q;
+    int64_t ldq;
+    uint8_t *scales;
+    int64_t lds;
+} mxfp4_quant_out_t;
+
+/*
+ * mxfp4_quantize_dual -- both quantizations of one tensor from a single read of it.
+ *
+ * Defined by: the operand transform of the Methodology section, as for mxfp4_quantize. That
+ * section runs all three GEMMs in MXFP4, so each of X, W and dY is a contraction operand along
+ * both of its axes (X: Fprop along K, Wgrad along the tokens; W: Fprop along K, Dgrad along N;
+ * dY: Dgrad along N, Wgrad along the tokens). This call writes both from one pass over x and is
+ * bit-identical to the two calls
+ *   mxfp4_quantize(x, dtype, rows, cols, ldx, 1, hadamard, <out_axis1 fields>, stream) and
+ *   mxfp4_quantize(x, dtype, rows, cols, ldx, 0, hadamard, <out_axis0 fields>, stream).
+ * Requirements: those of both calls (so rows % 32 == 0 and cols % 32 == 0); the two outputs must
+ * not overlap each other or x. Per bf16 element it reads 2 bytes instead of 4.
+ */
+mxfp4_status_t mxfp4_quantize_dual(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                   int64_t ldx, int hadamard, const mxfp4_quant_out_t *out_axis1,
+                                   const mxfp4_quant_out_t *out_axis0, void *stream);
 
 /*
  * mxfp4_gemm -- block-scaled FP4 GEMM with FP32 accumulation and output.

@@ -36,6 +36,13 @@ class Mxfp4Error(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, _status_string(status), status))
 
 
+class QuantOut(ctypes.Structure):
+    """mxfp4_quant_out_t: one output of mxfp4_quantize_dual."""
+    _fields_ = [("rounding", ctypes.c_int), ("seed", ctypes.c_uint64), ("stream_id", ctypes.c_uint32),
+                ("layout", ctypes.c_int), ("q", ctypes.c_void_p), ("ldq", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("lds", ctypes.c_int64)]
+
+
 class LinearCfg(ctypes.Structure):
     _fields_ = [("hadamard", ctypes.c_int), ("rnd_a", ctypes.c_int), ("rnd_b", ctypes.c_int),
                 ("seed", ctypes.c_uint64)]
@@ -57,6 +64,9 @@ def lib():
     i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
     L.mxfp4_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, u64, u32, ci, vp, i64, vp, i64, vp]
     L.mxfp4_quantize.restype = ci
+    L.mxfp4_quantize_dual.argtypes = [vp, ci, i64, i64, i64, ci, ctypes.POINTER(QuantOut),
+                                      ctypes.POINTER(QuantOut), vp]
+    L.mxfp4_quantize_dual.restype = ci
     L.mxfp4_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64,
                              ci, vp, ctypes.c_size_t, vp]
     L.mxfp4_gemm.restype = ci
@@ -154,6 +164,45 @@ def quantize(x, axis=1, hadamard=16, rounding="rne", seed=0, stream_id=0, q=None
                               scales.stride(0) if scales.dim() == 2 else 0, _stream(stream))
     _check(st, "mxfp4_quantize")
     return q, scales
+
+
+def _dual_out(x, spec, axis):
+    """Output buffers and mxfp4_quant_out_t for one axis of quantize_dual."""
+    spec = dict(spec or {})
+    lay = _layout(spec.get("layout", "rows"))
+    rows, cols = x.shape
+    L, outer = (cols, rows) if axis == 1 else (rows, cols)
+    padded = (outer + 255) // 256 * 256 if lay == TILED else outer
+    q = spec.get("q")
+    s = spec.get("scales")
+    if q is None:
+        q = torch.empty((padded, L // 2), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((padded, L // 32), dtype=torch.uint8, device=x.device)
+    out = QuantOut(_rounding(spec.get("rounding", "rne")), int(spec.get("seed", 0)) & (2 ** 64 - 1),
+                   int(spec.get("stream_id", 0)), lay, q.data_ptr(), q.stride(0) if q.dim() == 2 else 0,
+                   s.data_ptr(), s.stride(0) if s.dim() == 2 else 0)
+    return q, s, out
+
+
+def quantize_dual(x, hadamard=16, axis1=None, axis0=None, stream=None):
+    """Both quantizations of x in one pass: along each row (axis1) and along each column (axis0,
+    the quantized transpose). axis1 / axis0 are dicts with the optional keys rounding, seed,
+    stream_id, layout, q, scales, meaning what quantize() takes. Returns (q1, s1, q0, s0),
+    bit-identical to quantize(x, 1, ...) and quantize(x, 0, ...)."""
+    _require_cuda(x, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    dtype = {torch.bfloat16: BF16, torch.float32: F32}.get(x.dtype)
+    if dtype is None:
+        raise TypeError("x must be bfloat16 or float32")
+    q1, s1, o1 = _dual_out(x, axis1, 1)
+    q0, s0, o0 = _dual_out(x, axis0, 0)
+    rows, cols = x.shape
+    st = lib().mxfp4_quantize_dual(x.data_ptr(), dtype, rows, cols, x.stride(0), hadamard,
+                                   ctypes.byref(o1), ctypes.byref(o0), _stream(stream))
+    _check(st, "mxfp4_quantize_dual")
+    return q1, s1, q0, s0
 
 
 def gemm_workspace_bytes(M, N, K) -> int:

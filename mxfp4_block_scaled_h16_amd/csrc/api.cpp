@@ -212,6 +212,27 @@ mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
     return from_hip(e);
 }
 
+mxfp4_status_t mxfp4_quantize_dual(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                   int64_t ldx, int hadamard, const mxfp4_quant_out_t *out_axis1,
+                                   const mxfp4_quant_out_t *out_axis0, void *stream)
+{
+    if (!out_axis1 || !out_axis0) return MXFP4_ERR_NULL;
+    const mxfp4_quant_out_t &a = *out_axis1, &b = *out_axis0;
+    mxfp4_status_t st = check_quantize(x, dtype, rows, cols, ldx, 1, hadamard, a.rounding, a.layout,
+                                       a.q, a.ldq, a.scales, a.lds);
+    if (st == MXFP4_OK)
+        st = check_quantize(x, dtype, rows, cols, ldx, 0, hadamard, b.rounding, b.layout, b.q, b.ldq,
+                            b.scales, b.lds);
+    if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    const auto conv = [](const mxfp4_quant_out_t &o) {
+        return mx::QuantOut{o.rounding == MXFP4_SR_PHILOX, o.seed, o.stream_id, o.layout == MXFP4_LAYOUT_TILED,
+                            o.q, o.ldq, o.scales, o.lds};
+    };
+    return from_hip(mx::launch_quantize_dual(x, dtype == MXFP4_IN_F32, rows, cols, ldx, hadamard, conv(a),
+                                             conv(b), (hipStream_t)stream));
+}
+
 mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
                           int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,

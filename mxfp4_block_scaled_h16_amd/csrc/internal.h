@@ -18,6 +18,25 @@ hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t c
                                 bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream);
 
+// One output of launch_quantize_dual: the same arguments launch_quantize_rows/cols take.
+struct QuantOut {
+    bool stochastic;
+    uint64_t seed;
+    uint32_t stream_id;
+    bool tiled;
+    uint8_t *q;
+    int64_t ldq;
+    uint8_t *scales;
+    int64_t lds;
+};
+
+// Both quantizations of x[rows][cols] from one read: axis1 = launch_quantize_rows' output,
+// axis0 = launch_quantize_cols' output, bit-identical to the two separate launches.
+// Requires rows % 32 == 0 and cols % 32 == 0 (and the tiled outputs' lengths % 512 == 0).
+hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
+                                int hadamard, const QuantOut &axis1, const QuantOut &axis0,
+                                hipStream_t stream);
+
 // tiled: both operands in the tiled layout (K % 512 == 0, rows padded to multiples of 256);
 // otherwise row-major with leading dimensions. A workspace of gemm_workspace_bytes() bytes
 // (16-byte aligned) lets a GEMM with few output tiles split K (gemm_splits() ways) into FP32

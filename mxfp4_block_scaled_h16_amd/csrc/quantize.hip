@@ -259,6 +259,215 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     }
 }
 
+// ------------------------------------------------------------------------------ quant_dual --
+// Both quantizations of one tensor from a single read of it: along each row (axis 1) and along
+// each column (axis 0, written as the quantized transpose). Across Fprop, Dgrad and Wgrad each of
+// X, W and dY is a contraction operand along both of its axes, so a training step needs both.
+// A workgroup takes a 128 x 128-element tile:
+//  1. a lane loads 8 consecutive elements of a row (16 lanes per row, 4 rows per wavefront
+//     load), keeps the raw bits in an LDS tile and quantizes them along the row as quant_rows
+//     does (in-register and quad-crossing Hadamard stages, quad amax, one code word per lane);
+//  2. after a barrier a lane reads two columns of one 32-row block (one 32-bit LDS word per row;
+//     the 64 lanes of a wavefront read one 256-byte row, all banks distinct), rotates, scales
+//     and encodes them as quant_cols does and puts the codes into an LDS staging area in the
+//     output's byte order;
+//  3. after a second barrier the column output leaves as whole 1 KB tiled blocks (or as 16-byte
+//     pieces of 64-byte row segments in the rows layout).
+// Per bf16 element: 2 bytes read once, 2 x (0.5 + 1/32) bytes written.
+constexpr int kDualTile = 128;
+
+struct DualOut {
+    uint8_t *q;
+    int64_t ldq;
+    uint8_t *scales;
+    int64_t lds;
+    uint32_t key0, key1, stream_id;
+    uint32_t sr, tiled;
+};
+
+template <int H, bool F32>
+__global__ __launch_bounds__(kThreads) void quant_dual_kernel(
+    const void *__restrict__ x, int64_t ldx, uint32_t rows, uint32_t cols, uint32_t col_tiles,
+    DualOut o1, DualOut o0)
+{
+    constexpr int kEsize = F32 ? 4 : 2;
+    constexpr int kRowBytes = kDualTile * kEsize;
+    constexpr int kParts = F32 ? 2 : 1;           // 16-byte pieces per 8-element group
+    constexpr int kSteps = kDualTile / 16;        // row loads per lane
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kDualTile * kRowBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t out[kDualTile * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t out_scales[kDualTile * 4];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t c0 = (blockIdx.x % col_tiles) * kDualTile;
+    const uint32_t r0 = (blockIdx.x / col_tiles) * kDualTile;
+    const uint32_t nrows = min((uint32_t)kDualTile, rows - r0);  // multiples of 32
+    const uint32_t ncols = min((uint32_t)kDualTile, cols - c0);
+    const char *xb = reinterpret_cast<const char *>(x);
+
+    // 1. load, keep, quantize along the rows
+    {
+        const uint32_t gi = lane % 16;          // 8-element group within the tile row
+        const bool col_live = gi * 8 < ncols;   // a quad (one MX block) lives or dies whole
+        const bool upper1 = lane & 1, upper2 = lane & 2;
+        // a lane outside the tensor loads an element inside it instead (row and group clamped):
+        // the loads stay unconditional, and whatever it computes from them is never stored
+        const uint32_t lg = min(gi, ncols / 8u - 1u);
+        u32x4 raw[kSteps][kParts];
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k) {
+            const uint32_t lr = min(16u * k + 4u * wave + lane / 16u, nrows - 1u);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(xb + ((int64_t)(r0 + lr) * ldx + c0 + 8 * lg) * kEsize);
+#pragma unroll
+            for (int p = 0; p < kParts; ++p) raw[k][p] = __builtin_nontemporal_load(src + p);
+        }
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k) {
+            const uint32_t tr = 16 * k + 4 * wave + lane / 16;
+            u32x4 *dst = reinterpret_cast<u32x4 *>(tile + tr * kRowBytes + gi * 8 * kEsize);
+#pragma unroll
+            for (int p = 0; p < kParts; ++p) dst[p] = raw[k][p];
+        }
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k) {
+            const uint32_t tr = 16 * k + 4 * wave + lane / 16;
+            float v[8];
+            if constexpr (F32) {
+                const uint32_t w[8] = {raw[k][0].x, raw[k][0].y, raw[k][0].z, raw[k][0].w,
+                                       raw[k][1].x, raw[k][1].y, raw[k][1].z, raw[k][1].w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+            } else {
+                const uint32_t w[4] = {raw[k][0].x, raw[k][0].y, raw[k][0].z, raw[k][0].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    v[2 * u] = bf16_lo(w[u]);
+                    v[2 * u + 1] = bf16_hi(w[u]);
+                }
+            }
+            if constexpr (H >= 16) {
+                fwht_regs<8>(v);
+                fwht_cross_stage<1>(v, upper1);
+                if constexpr (H == 32) fwht_cross_stage<2>(v, upper2);
+            }
+            uint32_t amax = 0u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = max(amax, abs_bits(v[i]));
+            amax = max(amax, quad_xor<1>(amax));
+            amax = max(amax, quad_xor<2>(amax));
+            const uint32_t sc = e8m0_from_amax_bits(amax);
+            const uint32_t o = r0 + tr, g = c0 / 8 + gi;   // quantized row, global group
+            uint32_t word;
+            if (o1.sr) {
+                word = encode8_stochastic(v, sc, (uint64_t)o * cols + 8u * g, o1.key0, o1.key1, o1.stream_id);
+            } else {
+                prescale_if_zero_scale<8>(v, sc);
+                word = encode8_nearest(v, e8m0_divisor(sc));
+            }
+            if (sc == 0xFFu) word = 0u;
+            if (col_live && tr < nrows) {
+                if (o1.tiled) {
+                    const int64_t at = tiled_chunk(o, g / 4, cols) + 4 * (g % 4);
+                    __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(o1.q + at));
+                    if ((lane & 3u) == 0u) o1.scales[tiled_scale(o, g / 4, cols)] = (uint8_t)sc;
+                } else {
+                    __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(o1.q + (int64_t)o * o1.ldq) + g);
+                    if ((lane & 3u) == 0u) o1.scales[(int64_t)o * o1.lds + g / 4] = (uint8_t)sc;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // 2. quantize along the columns: wavefront w takes the 32-row block w, a lane two columns
+    {
+        const uint32_t blk = wave;
+        float v[2][32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const uint8_t *rowp = tile + (32 * blk + i) * kRowBytes + 4 * lane;
+            if constexpr (F32) {
+                v[0][i] = *reinterpret_cast<const float *>(rowp);
+                v[1][i] = *reinterpret_cast<const float *>(rowp + 256);
+            } else {
+                const uint32_t w = *reinterpret_cast<const uint32_t *>(rowp);
+                v[0][i] = bf16_lo(w);
+                v[1][i] = bf16_hi(w);
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const uint32_t tc = F32 ? lane + 64 * cc : 2 * lane + cc;  // tile column = quantized row
+            rotate_block<H>(v[cc]);
+            uint32_t amax = 0u;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[cc][i]));
+            const uint32_t sc = e8m0_from_amax_bits(amax);
+            uint32_t words[4];
+            if (o0.sr) {
+                const uint64_t index0 = (uint64_t)(c0 + tc) * rows + r0 + 32 * blk;
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd)
+                    words[wd] = encode8_stochastic(v[cc] + 8 * wd, sc, index0 + 8 * wd, o0.key0, o0.key1, o0.stream_id);
+            } else {
+                prescale_if_zero_scale<32>(v[cc], sc);
+                const float div = e8m0_divisor(sc);
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) words[wd] = encode8_nearest(v[cc] + 8 * wd, div);
+            }
+            if (sc == 0xFFu) words[0] = words[1] = words[2] = words[3] = 0u;
+            // tiled: 16-row slab, 64 bytes per row, chunk swizzled by (row % 16) / 4; the tile's
+            // four blocks are chunks 0..3 of one 128-element slice (r0 is a multiple of 128)
+            const uint32_t at = o0.tiled ? (tc / 16) * 1024 + (tc % 16) * 64 + 16 * (blk ^ ((tc % 16) / 4))
+                                         : tc * 64 + 16 * blk;
+            *reinterpret_cast<u32x4 *>(out + at) = u32x4{words[0], words[1], words[2], words[3]};
+            out_scales[tc * 4 + blk] = (uint8_t)sc;
+        }
+    }
+    __syncthreads();
+
+    // 3. store the column output
+    if (o0.tiled) {
+        // rows % 512 == 0 here, so the tile has all four blocks; one 1 KB block per 16-row slab
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const uint32_t s = 4 * pass + wave;
+            if (16 * s < ncols) {
+                const u32x4 t = *reinterpret_cast<const u32x4 *>(out + s * 1024 + lane * 16);
+                uint8_t *dst = o0.q + ((int64_t)(c0 / 16 + s) * (rows / 128) + r0 / 128) * 1024 + lane * 16;
+                __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(dst));
+            }
+        }
+        if (tid < ncols) {
+            // the four scale bytes of quantized row o are adjacent (block r0/32 is a multiple of 4)
+            const uint32_t o = c0 + tid;
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(out_scales + tid * 4);
+            *reinterpret_cast<uint32_t *>(o0.scales + tiled_scale(o, r0 / 32, rows)) = w;
+        }
+    } else {
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const uint32_t tc = 64 * pass + tid / 4, blk = tid % 4;
+            if (tc < ncols && 32 * blk < nrows) {
+                const u32x4 t = *reinterpret_cast<const u32x4 *>(out + tc * 64 + 16 * blk);
+                const int64_t o = c0 + tc;
+                __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(o0.q + o * o0.ldq + (r0 / 32 + blk) * 16));
+                o0.scales[o * o0.lds + r0 / 32 + blk] = out_scales[tc * 4 + blk];
+            }
+        }
+    }
+}
+
+template <int H, bool F32>
+hipError_t dual_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, const DualOut &o1,
+                         const DualOut &o0, hipStream_t stream)
+{
+    const int64_t col_tiles = (cols + kDualTile - 1) / kDualTile;
+    const int64_t row_tiles = (rows + kDualTile - 1) / kDualTile;
+    return launch(quant_dual_kernel<H, F32>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0, stream,
+                  x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles, o1, o0);
+}
+
 template <int H, bool F32, bool SR, bool TILED>
 hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
@@ -337,6 +546,26 @@ hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t c
 {
     return pick<ColsSel>(hadamard, f32, stochastic, tiled, x, rows, cols, ldx, seed, stream_id, q, ldq,
                          scales, lds, stream);
+}
+
+hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
+                                int hadamard, const QuantOut &axis1, const QuantOut &axis0,
+                                hipStream_t stream)
+{
+    const auto conv = [](const QuantOut &o) {
+        return DualOut{o.q, o.ldq, o.scales, o.lds, (uint32_t)o.seed, (uint32_t)(o.seed >> 32), o.stream_id,
+                       o.stochastic ? 1u : 0u, o.tiled ? 1u : 0u};
+    };
+    const DualOut o1 = conv(axis1), o0 = conv(axis0);
+    switch (hadamard * 2 + (f32 ? 1 : 0)) {
+    case 0: return dual_dispatch<0, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 1: return dual_dispatch<0, true>(x, rows, cols, ldx, o1, o0, stream);
+    case 32: return dual_dispatch<16, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 33: return dual_dispatch<16, true>(x, rows, cols, ldx, o1, o0, stream);
+    case 64: return dual_dispatch<32, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 65: return dual_dispatch<32, true>(x, rows, cols, ldx, o1, o0, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace mx

@@ -30,6 +30,7 @@ def test_header_declares_the_boundary():
                      "mxfp4_abi_version"):
         assert expected in names
     assert "mxfp4_tiled_sizes" in names and "mxfp4_gemm_workspace_bytes" in names
+    assert "mxfp4_quantize_dual" in names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 2
+    assert L.mxfp4_abi_version() == 3
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -59,6 +60,32 @@ def test_workspace_bytes(L):
 def _q(L, x=1 << 12, dtype=0, rows=64, cols=64, ldx=64, axis=1, h=16, rnd=0, q=1 << 12, ldq=32,
        s=1 << 12, lds=2, layout=0):
     return L.mxfp4_quantize(x, dtype, rows, cols, ldx, axis, h, rnd, 0, 0, layout, q, ldq, s, lds, None)
+
+
+def _dual(L, x=1 << 12, dtype=0, rows=64, cols=64, ldx=64, h=16, out1=None, out0=None, null1=False):
+    import mxfp4_block_scaled_h16_amd as mx
+    base = dict(rounding=0, seed=0, stream_id=0, layout=0, q=1 << 12, ldq=32, scales=1 << 12, lds=2)
+    o1 = mx.QuantOut(**dict(base, **(out1 or {})))
+    o0 = mx.QuantOut(**dict(base, **(out0 or {})))
+    return L.mxfp4_quantize_dual(x, dtype, rows, cols, ldx, h, None if null1 else ctypes.byref(o1),
+                                 ctypes.byref(o0), None)
+
+
+def test_quantize_dual_argument_errors(L):
+    # each output is validated as the matching mxfp4_quantize call would be
+    assert _dual(L, null1=True) == 1
+    assert _dual(L, rows=48) == 2                          # axis-0 length (rows) % 32
+    assert _dual(L, cols=48, ldx=48) == 2                  # axis-1 length (cols) % 32
+    assert _dual(L, h=8) == 3
+    assert _dual(L, out1=dict(rounding=4)) == 3
+    assert _dual(L, out0=dict(layout=7)) == 3
+    assert _dual(L, out0=dict(ldq=16)) == 3                # ldq < rows/2 for the transpose
+    assert _dual(L, out1=dict(ldq=40)) == 4                # ldq % 16
+    assert _dual(L, out0=dict(q=None)) == 1
+    assert _dual(L, out1=dict(layout=1)) == 2              # tiled axis-1 output needs cols % 512
+    assert _dual(L, rows=512, cols=64, out0=dict(layout=1, scales=(1 << 12) + 4)) == 4  # tiled scales 16-B
+    assert _dual(L, x=(1 << 12) + 2) == 4
+    assert _dual(L, rows=0) == 0 and _dual(L, cols=0, x=None) == 0
 
 
 def test_quantize_argument_errors(L):
