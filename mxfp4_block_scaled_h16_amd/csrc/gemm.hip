@@ -113,7 +113,11 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
 //  * LDS fragment and scale reads for the next 64-wide sub-step are issued between the MFMAs of
 //    the current one, and so are the DMA instructions;
 //  * the product is formed transposed (B as the MFMA's first operand), so each lane ends with
-//    four consecutive output columns per register quad and stores 16 bytes at a time.
+//    four consecutive output columns per register quad;
+//  * the epilogue stages each wavefront's result through LDS in 32-row slices, so that every
+//    store instruction writes whole row segments (whole 128-byte lines) instead of 32-byte
+//    pieces of 32 rows: the FP32 output is the largest HBM stream of the kernel and its writes
+//    all come at once, when every CU finishes its tile.
 // Rows of a stage buffer hold their four 16-byte chunks XOR-permuted by bits 2-3 of the row: the
 // LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, 64 banks) at a time, and the 16 rows
 // those lanes read then land in 16 distinct bank groups.
@@ -423,6 +427,40 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
         alpha = 1.0f;
     }
     const bool full_cols = n0 + kBN <= N && (ldc % 4) == 0 && ((uintptr_t)c % 16) == 0;
+    if (full_cols) {
+        // stage each 32-row slice of this wavefront's 128 x kWaveCols result through LDS so that
+        // a store instruction writes whole rows (two rows of kWaveCols floats)
+        constexpr int kEpiRow = G::kWaveCols * 4 + 16;   // bytes per staged row (padded)
+        constexpr int kEpiWave = 32 * kEpiRow;           // one slice per wavefront
+        constexpr int kLanesPerRow = G::kWaveCols / 4;   // 16-byte pieces per row
+        constexpr int kRowsPerStore = 64 / kLanesPerRow;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();                    // every wavefront is done with the stages
+        __builtin_amdgcn_sched_barrier(0);
+        uint8_t *epi = lds + wave * kEpiWave;
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < FJ; ++jj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4v v = {acc[i][jj][4 * q + 0], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
+                                      acc[i][jj][4 * q + 3]};
+                    *reinterpret_cast<f32x4v *>(epi + r * kEpiRow + (32 * jj + 8 * q + 4 * half) * 4) = v;
+                }
+#pragma unroll
+            for (int p = 0; p < 32 / kRowsPerStore; ++p) {
+                const int rr = kRowsPerStore * p + lane / kLanesPerRow;
+                const int cc = 4 * (lane % kLanesPerRow);
+                f32x4v v = *reinterpret_cast<const f32x4v *>(epi + rr * kEpiRow + cc * 4);
+                v = v * alpha;
+                const int m = m0 + wm * 128 + 32 * i + rr;
+                if (m < M)
+                    *reinterpret_cast<f32x4v *>(c + (int64_t)m * ldc + n0 + wn * G::kWaveCols + cc) = v;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
         const int m = m0 + wm * 128 + 32 * i + r;
