@@ -121,11 +121,11 @@ __device__ __forceinline__ uint32_t e2m1_stochastic(float a, uint32_t r)
     const uint32_t lo = ge1 ? (A >> 22) - 252u : (ge_half ? 1u : 0u);
     const uint32_t t = ge1 ? (A << 10) : (ge_half ? (A << 9) : t_small);
     const uint32_t mag = lo + (r < t ? 1u : 0u);
-    return A >= 0x40C00000u ? 7u : mag;  // a >= 6 (or NaN, whose block is discarded)
+    // the block scale keeps a below 8, so a in [6, 8) has lo = 7 and saturates here (a NaN or
+    // infinity also lands on 7, in a block whose codes are discarded)
+    return min(mag, 7u);
 }
 
-// Sign of a binary32 value as the E2M1 sign bit (bit 3).
-__device__ __forceinline__ uint32_t sign_nibble(float y) { return (__float_as_uint(y) >> 28) & 8u; }
 
 // ---------------------------------------------------------------------------- Philox4x32-10 --
 // Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten rounds;
@@ -142,8 +142,9 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     for (int round = 0; round < 10; ++round) {
         const uint64_t p = (uint64_t)0xD2511F53u * c0;
         const uint64_t q = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(q >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p >> 32) ^ c3 ^ k1;
+        // three-input XORs (truth table 0x96) in one gfx950 bitop3 instruction each
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(q >> 32), c1, k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p >> 32), c3, k1, 0x96);
         c1 = (uint32_t)q;
         c3 = (uint32_t)p;
         c0 = n0;
@@ -171,13 +172,15 @@ __device__ __forceinline__ uint32_t encode8_stochastic(const float *y, uint32_t 
     const Philox4 r0 = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), stream_id, 0u, key0, key1);
     const uint64_t c1 = c + 1;
     const Philox4 r1 = philox4x32_10((uint32_t)c1, (uint32_t)(c1 >> 32), stream_id, 0u, key0, key1);
-    uint32_t word = 0u;
+    uint32_t word = 0u, signs = 0u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const uint32_t rnd = e < 4 ? r0.w[e] : r1.w[e - 4];
-        word |= (e2m1_stochastic(fabsf(y[e] * mul), rnd) | sign_nibble(y[e])) << (4 * e);
+        word |= e2m1_stochastic(fabsf(y[e] * mul), rnd) << (4 * e);
+        // sign bit of y[e] to bit 4 e + 3 (the sign of the rotated value, also for zeros)
+        signs |= (__float_as_uint(y[e]) >> (28 - 4 * e)) & (8u << (4 * e));
     }
-    return word;
+    return word | signs;
 }
 
 // ---------------------------------------------------------------------------- cross-lane ------

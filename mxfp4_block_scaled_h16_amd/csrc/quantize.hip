@@ -269,8 +269,9 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 //     does (in-register and quad-crossing Hadamard stages, quad amax, one code word per lane);
 //  2. after a barrier a lane reads two columns of one 32-row block (one 32-bit LDS word per row;
 //     the 64 lanes of a wavefront read one 256-byte row, all banks distinct), rotates, scales
-//     and encodes them as quant_cols does and puts the codes into an LDS staging area in the
-//     output's byte order;
+//     and encodes them as quant_cols does; after a barrier (every lane holds its columns) the
+//     codes go into the front of the same LDS tile, in the output's byte order, so that a
+//     workgroup needs only the 32 KB tile (4 workgroups per CU for bf16);
 //  3. after a second barrier the column output leaves as whole 1 KB tiled blocks (or as 16-byte
 //     pieces of 64-byte row segments in the rows layout).
 // Per bf16 element: 2 bytes read once, 2 x (0.5 + 1/32) bytes written.
@@ -295,8 +296,8 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
     constexpr int kParts = F32 ? 2 : 1;           // 16-byte pieces per 8-element group
     constexpr int kSteps = kDualTile / 16;        // row loads per lane
     __shared__ __attribute__((aligned(16))) uint8_t tile[kDualTile * kRowBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t out[kDualTile * 64];
-    __shared__ __attribute__((aligned(16))) uint8_t out_scales[kDualTile * 4];
+    uint8_t *out = tile;                          // reused once the tile has been read
+    uint8_t *out_scales = tile + kDualTile * 64;
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t c0 = (blockIdx.x % col_tiles) * kDualTile;
@@ -395,6 +396,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
                 v[1][i] = bf16_hi(w);
             }
         }
+        __syncthreads();
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const uint32_t tc = F32 ? lane + 64 * cc : 2 * lane + cc;  // tile column = quantized row
