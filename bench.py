@@ -39,6 +39,7 @@ LLAMA_INPUT = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "o_in", "gat
                "up": "mlp_in", "down": "down_in"}
 WORKLOADS = {
     "qkv": ("Llama-3.1-8B QKV projection Fprop+Dgrad+Wgrad", [("qkv", 4096, 6144)], "FDW", 8192),
+    "qkv_fprop": ("Llama-3.1-8B QKV projection Fprop", [("qkv", 4096, 6144)], "F", 8192),
     "small": ("single small layer Fprop+Dgrad+Wgrad", [("small", 512, 256)], "FDW", 256),
     "gateup": ("Llama-3.1-8B fused gate+up projection Fprop+Dgrad", [("gateup", 4096, 28672)], "FD", 8192),
     "down": ("Llama-3.1-8B down projection Wgrad", [("down", 14336, 4096)], "W", 8192),
@@ -54,6 +55,8 @@ def parse_args():
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="qkv")
     p.add_argument("--hadamard", type=int, default=16, choices=[0, 16, 32])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--settle", type=float, default=1.0,
+                   help="seconds of untimed steps before the warm-up (GPU clock ramp)")
     p.add_argument("--separate-quant", action="store_true",
                    help="one quantizer launch per axis instead of one dual launch per tensor")
     p.add_argument("--copy-calibration", action="store_true",
@@ -64,7 +67,7 @@ def parse_args():
 class Plan:
     """Buffers and the ordered launch list of one step (quantize and GEMM launches)."""
 
-    def __init__(self, mx, torch, workload, h, sets, dual=True):
+    def __init__(self, mx, torch, workload, h, sets, dual=True, host=None):
         import numpy as np
         from synth import inputs
         desc, projs, passes, M = WORKLOADS[workload]
@@ -74,7 +77,11 @@ class Plan:
         dev = "cuda"
         to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
         # host tensors (bf16 bit patterns), drawn by the shared seeded recipe
-        if workload == "layer":
+        if host is not None:
+            acts, per_proj = host["acts"], host["proj"]
+            self.host = host
+            inp = {projs[0][0]: "x"}
+        elif workload == "layer":
             acts, per_proj = inputs.llama_layer_inputs(seed=0, tokens=M)
             self.host = {"acts": acts, "proj": per_proj}
             inp = LLAMA_INPUT
@@ -303,6 +310,99 @@ def cpu_baseline(plan, h):
             "step_seconds_projected": t_step}
 
 
+class TimingEvents:
+    """HIP timing events created with hipEventDisableSystemFence, recorded on the stream the
+    kernels run on. Recording a default event also writes back and invalidates the caches
+    (a system-scope fence), which after every launch adds several microseconds and flushes the
+    dirty output lines of the previous kernel; these events only take timestamps."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        # the HIP runtime already loaded by torch and libmxfp4
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self):
+        e = self.ct.c_void_p()
+        st = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % st)
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        st = self.hip.hipEventRecord(e, stream)
+        if st != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % st)
+
+    def elapsed_ms(self, a, b):
+        v = self.ct.c_float()
+        st = self.hip.hipEventElapsedTime(self.ct.byref(v), a, b)
+        if st != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % st)
+        return v.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+def settle(plan, seconds):
+    """Untimed steps until `seconds` of wall time have passed: the GPU leaves its idle clock
+    state only after some tens of milliseconds of sustained load (a cold start measured 10-15%
+    slower than the steady state of a training loop). Returns the number of steps run."""
+    import torch
+    n, t_end = 0, time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for f in plan.launches(n):
+            f()
+        n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def run_timed(plan, steps, warmup):
+    """W untimed warm-up steps, then EXACTLY K timed steps bracketed by device synchronizations
+    (host clock, no per-launch instrumentation), then K more steps with fence-free HIP events
+    around every launch on the launch stream for the per-kernel durations.
+    Returns (ms per step of the timed steps, average ms of each launch of the step)."""
+    import numpy as np
+    import torch
+    for s in range(warmup):
+        for f in plan.launches(s):
+            f()
+    calls = [plan.launches(s) for s in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for f in calls[s]:
+            f()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev = TimingEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    n_launch = len(plan.op_list)
+    marks = [[ev.create() for _ in range(n_launch + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        ev.record(marks[s][0], stream)
+        for i, f in enumerate(calls[s]):
+            f()
+            ev.record(marks[s][i + 1], stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([[ev.elapsed_ms(marks[s][i], marks[s][i + 1]) for i in range(n_launch)]
+                           for s in range(steps)])
+    ev.close()
+    return (t1 - t0) * 1e3 / steps, per_launch.mean(0)
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -324,31 +424,8 @@ def main():
     plan = Plan(mx, torch, args.workload, h, sets, dual=not args.separate_quant)
     torch.cuda.synchronize()
 
-    for s in range(args.warmup):
-        for f in plan.launches(s):
-            f()
-    torch.cuda.synchronize()
-
-    # timed region: K steps, per-launch HIP events on the stream the kernels run on
-    stream = torch.cuda.current_stream()
-    n_launch = len(plan.op_list)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)] for _ in range(args.steps)]
-    calls = [plan.launches(s) for s in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev = events[s]
-        ev[0].record(stream)
-        for i, f in enumerate(calls[s]):
-            f()
-            ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    per_launch = np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(n_launch)]
-                           for s in range(args.steps)])  # ms
-    avg_ms = per_launch.mean(0)
+    settle_steps = settle(plan, args.settle)
+    ms_per_step, avg_ms = run_timed(plan, args.steps, args.warmup)
     step_flops = sum(w for _, kind, _, w in plan.op_list if kind == "gemm")
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -378,6 +455,22 @@ def main():
                  "bytes_per_elem": {"single": QUANT_BYTES_PER_ELEM, "dual": DUAL_BYTES_PER_ELEM},
                  "launches": "dual" if plan.dual else "separate", "us_per_step": round(q_s * 1e6, 1)}
 
+    # the Fprop configuration taken literally (X and W along K, nearest rounding, one GEMM), timed
+    # in the same run on the same inputs
+    fprop = None
+    if args.workload == "qkv" and "F" in passes:
+        fplan = Plan(mx, torch, "qkv_fprop", h, sets, dual=False, host=plan.host)
+        settle(fplan, min(args.settle, 0.25))
+        f_ms, f_avg = run_timed(fplan, args.steps, args.warmup)
+        f_flops = sum(w for _, kind, _, w in fplan.op_list if kind == "gemm")
+        f_gemm_s = sum(float(t) * 1e-3 for (_, kind, _, _), t in zip(fplan.op_list, f_avg) if kind == "gemm")
+        f_q_s = sum(float(t) * 1e-3 for (_, kind, _, _), t in zip(fplan.op_list, f_avg) if kind != "gemm")
+        fprop = {"workload": "Llama-3.1-8B QKV projection Fprop only, M=8192 K=4096 N=6144, H%d, MXFP4 RNE" % h,
+                 "ms_per_step": round(f_ms, 4), "tflops": round(f_flops / (f_ms * 1e-3) / 1e12, 1),
+                 "gemm_tflops": round(f_flops / f_gemm_s / 1e12, 1), "quant_us": round(f_q_s * 1e6, 1),
+                 "launches": [label for label, _, _, _ in fplan.op_list]}
+        del fplan
+
     if args.copy_calibration:
         buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         buf2 = torch.empty_like(buf)
@@ -395,8 +488,13 @@ def main():
         "config": {"workload": "%s, M=%d tokens, %s, H%d, MXFP4 RNE (Philox SR on Wgrad operands)"
                                % (desc, M, sizes, h),
                    "M": M, "hadamard": h, "passes": passes, "input_sets": sets},
+        "timing": {"settle_s": args.settle, "settle_steps": settle_steps,
+                   "value": "host clock over the K timed steps, no per-launch instrumentation",
+                   "kernels": "a second pass of K steps with fence-free HIP events around every launch"},
         "roofline": roofline, "quantizer": quantizer, "kernels": kernels, "cpu_baseline": cpu,
     }
+    if fprop is not None:
+        line["fprop_only"] = fprop
     print(json.dumps(line), flush=True)
     return 0
 
