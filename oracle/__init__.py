@@ -42,6 +42,8 @@ def _load():
     lib.oracle_philox4x32_10.restype = None
     lib.oracle_fwht_binary32.argtypes = [vp, i64, c_int]
     lib.oracle_fwht_binary32.restype = None
+    lib.oracle_rht_signs.argtypes = [u64, i64, vp]
+    lib.oracle_rht_signs.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = c_int
     _lib = lib
@@ -54,6 +56,7 @@ def _ptr(a):
 
 RNE = 0
 SR = 1
+RHT = 0x100  # added to hadamard (16 or 32): randomized Hadamard, signs keyed by the seed
 
 
 def num_threads() -> int:
@@ -76,8 +79,16 @@ def fwht(v, h):
     return a.reshape(np.shape(v))
 
 
+def rht_signs(seed, count):
+    """The randomized-Hadamard diagonal d_0 .. d_{count-1} (+1 / -1) for key ``seed``."""
+    out = np.zeros(int(count), dtype=np.int8)
+    _load().oracle_rht_signs(int(seed) & (2 ** 64 - 1), int(count), _ptr(out))
+    return out
+
+
 def quantize(x, axis=1, hadamard=16, rounding=RNE, seed=0, stream=0):
-    """MXFP4-quantize a 2-D array along ``axis`` after the block Hadamard rotation.
+    """MXFP4-quantize a 2-D array along ``axis`` after the block Hadamard rotation
+    (``hadamard`` 16 or 32 plus ``RHT``: the randomized Hadamard with signs keyed by ``seed``).
 
     x: uint16 (bf16 bit patterns) or float32, shape (rows, cols).
     Returns (codes uint8 [outer, L/2], scales uint8 [outer, L/32]) with L the quantized length
@@ -144,8 +155,10 @@ def gemm_sampled(aq, as_, bq, bs, ms, ns, alpha=1.0):
 
 
 def alpha_for(hadamard):
-    """H_h H_h^T = h I, so a product of two rotated operands carries a factor h."""
-    return 1.0 / hadamard if hadamard else 1.0
+    """H_h H_h^T = h I (and (H D)(H D)^T = h I for a +-1 diagonal D), so a product of two
+    rotated operands carries a factor h."""
+    h = int(hadamard) & ~RHT
+    return 1.0 / h if h else 1.0
 
 
 # ------------------------------------------------------------------ the three linear GEMMs --

@@ -35,6 +35,13 @@
  *    r < f * 2^32, r being a 32-bit Philox word. Key = (seed mod 2^32, seed >> 32); for the
  *    element at position j of quantized row o (index i = o * L + j, L the quantized length),
  *    counter = (floor(i/4) mod 2^32, floor(i/4) >> 32, stream, 0), word i mod 4.
+ *  - Randomized Hadamard (the pages name it as the other rotation tried, without a construction):
+ *    y = H_h (d .* x) per aligned group, with d_j = -1 or +1 for position j along the quantized
+ *    axis -- the same for every quantized row, so two operands rotated with the same key keep
+ *    their product up to h. d_j = -1 iff bit (j mod 32) of word ((j / 32) mod 4) of
+ *    Philox4x32-10 with key (seed mod 2^32, seed >> 32) and counter (floor(j/128) mod 2^32,
+ *    floor(j/128) >> 32, 0, 1) is set (the last counter word 1 keeps it apart from the
+ *    stochastic-rounding words, whose last counter word is 0).
  *  - GEMM: C[m][n] = alpha * sum_k deq(A)[m][k] * deq(B)[n][k]; each 32-element block product is
  *    an exact integer sum, scaled exactly, and blocks are summed in binary64.
  *
@@ -149,6 +156,23 @@ static uint32_t sr_word(uint64_t seed, uint32_t stream, uint64_t i)
     return out[i & 3u];
 }
 
+/* Sign of the randomized-Hadamard diagonal at position j along the quantized axis: 1 = negate. */
+static int rht_negate(uint64_t seed, uint64_t j)
+{
+    uint64_t c = j >> 7;
+    uint32_t ctr[4] = {(uint32_t)c, (uint32_t)(c >> 32), 0u, 1u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return (int)((out[(j >> 5) & 3u] >> (j & 31u)) & 1u);
+}
+
+/* d_j for j = 0 .. count - 1 as +1 / -1 bytes. */
+void oracle_rht_signs(uint64_t seed, int64_t count, int8_t *out)
+{
+    for (int64_t j = 0; j < count; ++j) out[j] = rht_negate(seed, (uint64_t)j) ? (int8_t)-1 : (int8_t)1;
+}
+
 /* ---------------------------------------------------------------- Hadamard ------------------ */
 
 /* In-place unnormalised Walsh-Hadamard transform of h values in binary32 (h a power of two). */
@@ -187,14 +211,18 @@ static float load_element(const void *x, int dtype, int64_t r, int64_t c, int64_
  * axis = 1: along each row (L = cols), outputs q[rows][cols/2], scales[rows][cols/32].
  * axis = 0: along each column (L = rows), outputs the quantized transpose q[cols][rows/2],
  *           scales[cols][rows/32].
- * h in {0, 16, 32}; rounding 0 = nearest-even, 1 = stochastic (Philox). Returns 0 on success.
+ * h in {0, 16, 32}, or 16 / 32 plus 0x100 for the randomized Hadamard (signs keyed by seed);
+ * rounding 0 = nearest-even, 1 = stochastic (Philox). Returns 0 on success.
  */
 int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int axis,
                     int h, int rounding, uint64_t seed, uint32_t stream, uint8_t *q, uint8_t *scales)
 {
     const int64_t L = axis ? cols : rows;
     const int64_t outer = axis ? rows : cols;
+    const int randomized = (h & 0x100) != 0;
+    h &= ~0x100;
     if (L % 32 != 0 || (h != 0 && h != 16 && h != 32) || (axis != 0 && axis != 1)) return 1;
+    if (randomized && h == 0) return 1;
     int status = 0;
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t o = 0; o < outer; ++o) {
@@ -202,6 +230,9 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
         if (!y) { status = 2; continue; }
         for (int64_t j = 0; j < L; ++j)
             y[j] = axis ? load_element(x, dtype, o, j, ldx) : load_element(x, dtype, j, o, ldx);
+        if (randomized)
+            for (int64_t j = 0; j < L; ++j)
+                if (rht_negate(seed, (uint64_t)j)) y[j] = -y[j];  /* exact */
         if (h) oracle_fwht_binary32(y, L, h);
         for (int64_t b = 0; b < L / 32; ++b) {
             const float *blk = y + 32 * b;

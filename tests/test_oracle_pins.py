@@ -480,3 +480,60 @@ def test_rotation_lowers_error_on_outlier_activations():
     err = {h: np.linalg.norm(oracle.linear_fprop(xb, w, hadamard=h) - ref) / np.linalg.norm(ref)
            for h in (0, 16)}
     assert err[16] < err[0]
+
+
+# ----------------------------------------------------------------- randomized Hadamard ------
+
+@pytest.mark.parametrize("h", [16, 32])
+def test_rht_exact_construction(h):
+    """X = d .* (U H / h) blockwise, with d the oracle's own sign diagonal: the randomized
+    rotation must recover U exactly (lossless MXFP4) and the forward GEMM of two such operands
+    (same key) must equal the plain product X W^T. Applying d after H, indexing it by the outer
+    dimension, or giving the two operands different signs all break this."""
+    rng = np.random.default_rng(61)
+    M, N, K = 24, 40, 256
+    seed = 0xABCDEF12345
+    d = oracle.rht_signs(seed, K).astype(np.float64)
+    X, _ = _exact_rotated_operand(rng, M, K, h)
+    W, _ = _exact_rotated_operand(rng, N, K, h)
+    X, W = X * d, W * d
+    y = oracle.linear_fprop(X.astype(np.float32), W.astype(np.float32), hadamard=h | oracle.RHT, seed=seed)
+    assert np.allclose(y, X @ W.T, rtol=1e-12, atol=1e-12)
+    # a different key gives different signs, and the construction no longer holds exactly
+    y2 = oracle.linear_fprop(X.astype(np.float32), W.astype(np.float32), hadamard=h | oracle.RHT, seed=seed + 1)
+    assert not np.allclose(y2, X @ W.T, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_rht_is_h_of_sign_flipped_input(axis, rounding):
+    """Randomized rotation = deterministic rotation of the input with its sign bits flipped where
+    d_j = -1, j the position along the quantized axis (bf16 sign flips are exact)."""
+    rng = np.random.default_rng(62)
+    x = inputs.bf16_bits(rng.standard_normal((96, 160)).astype(np.float32))
+    x = x[:, :128] if axis == 1 else x[:96, :]
+    L = x.shape[1] if axis == 1 else x.shape[0]
+    seed = 77
+    d = oracle.rht_signs(seed, L)
+    flip = np.where(d < 0, 0x8000, 0).astype(np.uint16)
+    xf = x ^ (flip[None, :] if axis == 1 else flip[:, None])
+    for h in (16, 32):
+        a = oracle.quantize(x, axis, h | oracle.RHT, rounding, seed, 1)
+        b = oracle.quantize(xf, axis, h, rounding, seed, 1)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_rht_signs_balanced_and_keyed():
+    """The sign diagonal is a fair, key-dependent +-1 sequence: the count of -1 over 2^16
+    positions is within 5 standard deviations of half, two keys disagree on about half the
+    positions, and the same key reproduces the same signs."""
+    n = 1 << 16
+    a = oracle.rht_signs(1, n)
+    b = oracle.rht_signs(2, n)
+    assert set(np.unique(a)) <= {-1, 1}
+    sd = math.sqrt(n) / 2
+    assert abs(int((a < 0).sum()) - n / 2) < 5 * sd
+    assert abs(int((a != b).sum()) - n / 2) < 5 * sd
+    assert np.array_equal(a, oracle.rht_signs(1, n))
+    # prefixes agree: the sign of position j does not depend on how many are requested
+    assert np.array_equal(oracle.rht_signs(1, 200), a[:200])
