@@ -54,6 +54,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="qkv")
     p.add_argument("--hadamard", type=int, default=16, choices=[0, 16, 32])
+    p.add_argument("--rht", action="store_true",
+                   help="randomized Hadamard: a sign diagonal keyed by each GEMM's seed before H")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--settle", type=float, default=1.0,
                    help="seconds of untimed steps before the warm-up (GPU clock ramp)")
@@ -73,7 +75,8 @@ class Plan:
         desc, projs, passes, M = WORKLOADS[workload]
         self.mx, self.torch, self.h, self.passes, self.M = mx, torch, h, passes, M
         self.dual = dual
-        self.alpha = 1.0 / h if h else 1.0
+        # h may carry the randomized-Hadamard flag; alpha undoes the factor of the size alone
+        self.alpha = 1.0 / (h & ~mx.RHT) if h & ~mx.RHT else 1.0
         dev = "cuda"
         to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
         # host tensors (bf16 bit patterns), drawn by the shared seeded recipe
@@ -414,7 +417,12 @@ def main():
     import torch
     import mxfp4_block_scaled_h16_amd as mx
 
-    h = args.hadamard
+    if args.rht and args.hadamard == 0:
+        print("--rht needs --hadamard 16 or 32", file=sys.stderr)
+        return 2
+    h = args.hadamard | (mx.RHT if args.rht else 0)
+    hsize = args.hadamard
+    rot_name = ("RHT%d" if args.rht else "H%d") % hsize
     desc, projs, passes, M = WORKLOADS[args.workload]
     in_bytes = 0
     for name, K, N in projs:
@@ -465,7 +473,7 @@ def main():
         f_flops = sum(w for _, kind, _, w in fplan.op_list if kind == "gemm")
         f_gemm_s = sum(float(t) * 1e-3 for (_, kind, _, _), t in zip(fplan.op_list, f_avg) if kind == "gemm")
         f_q_s = sum(float(t) * 1e-3 for (_, kind, _, _), t in zip(fplan.op_list, f_avg) if kind != "gemm")
-        fprop = {"workload": "Llama-3.1-8B QKV projection Fprop only, M=8192 K=4096 N=6144, H%d, MXFP4 RNE" % h,
+        fprop = {"workload": "Llama-3.1-8B QKV projection Fprop only, M=8192 K=4096 N=6144, %s, MXFP4 RNE" % rot_name,
                  "ms_per_step": round(f_ms, 4), "tflops": round(f_flops / (f_ms * 1e-3) / 1e12, 1),
                  "gemm_tflops": round(f_flops / f_gemm_s / 1e12, 1), "quant_us": round(f_q_s * 1e6, 1),
                  "launches": [label for label, _, _, _ in fplan.op_list]}
@@ -485,9 +493,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
         "data": "synthetic",
-        "config": {"workload": "%s, M=%d tokens, %s, H%d, MXFP4 RNE (Philox SR on Wgrad operands)"
-                               % (desc, M, sizes, h),
-                   "M": M, "hadamard": h, "passes": passes, "input_sets": sets},
+        "config": {"workload": "%s, M=%d tokens, %s, %s, MXFP4 RNE (Philox SR on Wgrad operands)"
+                               % (desc, M, sizes, rot_name),
+                   "M": M, "hadamard": hsize, "randomized_hadamard": bool(args.rht), "passes": passes,
+                   "input_sets": sets},
         "timing": {"settle_s": args.settle, "settle_steps": settle_steps,
                    "value": "host clock over the K timed steps, no per-launch instrumentation",
                    "kernels": "a second pass of K steps with fence-free HIP events around every launch"},

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 3
+#define MXFP4_ABI_VERSION 4
 
 typedef enum {
     MXFP4_OK = 0,
@@ -68,6 +68,18 @@ typedef enum { MXFP4_IN_BF16 = 0, MXFP4_IN_F32 = 1 } mxfp4_dtype_t;
 typedef enum { MXFP4_RNE = 0, MXFP4_SR_PHILOX = 1 } mxfp4_rounding_t;
 
 typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
+
+/*
+ * Randomized Hadamard: OR this flag into a hadamard size of 16 or 32 (quantize, quantize_dual,
+ * linear cfg) to rotate y = H_h (d .* x) instead of y = H_h x. d_j = -1 or +1 for position j
+ * along the quantized axis, the same for every quantized row: d_j = -1 iff bit (j mod 32) of word
+ * ((j / 32) mod 4) of Philox4x32-10 with key (seed mod 2^32, seed >> 32) and counter
+ * (floor(j/128) mod 2^32, floor(j/128) >> 32, 0, 1). The two operands of one GEMM must use the
+ * same seed; the product then keeps the factor h (alpha = 1/h). Defined by: the Methodology
+ * section names randomized Hadamard rotations as the other rotation tried (and reports that it
+ * did not converge on the full pipeline); the construction is this library's reading.
+ */
+#define MXFP4_RHT 0x100
 
 /*
  * Memory layout of a quantized operand with `outer` quantized rows of length L.
@@ -103,7 +115,8 @@ mxfp4_status_t mxfp4_tiled_sizes(int64_t outer, int64_t L, size_t *codes_bytes, 
  *   axis=0   quantize along each column (L = rows) and write the quantized TRANSPOSE:
  *                                                  q[cols][ldq], scales[cols][lds]
  *            (the Wgrad token axis and the Dgrad weight operand).
- *   hadamard 0 (no rotation), 16 or 32; rounding MXFP4_RNE or MXFP4_SR_PHILOX with (seed, stream).
+ *   hadamard 0 (no rotation), 16 or 32, or 16 / 32 | MXFP4_RHT (randomized, signs keyed by seed);
+ *            rounding MXFP4_RNE or MXFP4_SR_PHILOX with (seed, stream).
  *   layout   MXFP4_LAYOUT_ROWS (q, ldq, scales, lds as above) or MXFP4_LAYOUT_TILED (see above).
  *
  * Requirements: rows, cols >= 0; L % 32 == 0; at most 2^30 32-element blocks (rows * cols / 32);
@@ -174,7 +187,7 @@ size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Per-operand configuration of one linear-layer GEMM. */
 typedef struct {
-    int hadamard;              /* 0, 16 or 32: rotation along the GEMM's contraction axis */
+    int hadamard;              /* 0, 16 or 32 (| MXFP4_RHT): rotation along the contraction axis */
     mxfp4_rounding_t rnd_a;    /* rounding of the first operand (X, dY, dY^T) */
     mxfp4_rounding_t rnd_b;    /* rounding of the second operand (W, W^T, X^T) */
     uint64_t seed;             /* Philox key for stochastic rounding; stream 0 = first operand,

@@ -14,7 +14,7 @@ import os
 import torch  # imported first: the library binds to the HIP runtime torch has loaded
 
 __all__ = [
-    "Mxfp4Error", "quantize", "gemm", "linear_fprop", "linear_dgrad", "linear_wgrad",
+    "Mxfp4Error", "RHT", "quantize", "quantize_dual", "gemm", "linear_fprop", "linear_dgrad", "linear_wgrad",
     "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD", "ROWS", "TILED",
     "tiled_sizes", "gemm_workspace_bytes",
 ]
@@ -26,6 +26,7 @@ RNE, SR = 0, 1
 FPROP, DGRAD, WGRAD = 0, 1, 2
 ROWS, TILED = 0, 1
 BF16, F32 = 0, 1
+RHT = 0x100  # OR into hadamard (16 or 32): randomized Hadamard, signs keyed by the seed
 
 _lib = None
 

@@ -36,6 +36,16 @@ mxfp4_status_t check_device()
 mxfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_LAUNCH; }
 
 // Validation of one quantize call; also used by the linear entry points.
+static_assert(MXFP4_RHT == mx::kRandomizedHadamard, "randomized-Hadamard flag");
+
+// hadamard: 0, 16 or 32, or 16 / 32 with MXFP4_RHT
+bool valid_rotation(int hadamard)
+{
+    const int h = hadamard & ~MXFP4_RHT;
+    if (h != 0 && h != 16 && h != 32) return false;
+    return !((hadamard & MXFP4_RHT) && h == 0);
+}
+
 mxfp4_status_t check_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
                               int64_t ldx, int axis, int hadamard, mxfp4_rounding_t rounding,
                               mxfp4_layout_t layout, const uint8_t *q, int64_t ldq,
@@ -45,7 +55,7 @@ mxfp4_status_t check_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
     const bool tiled = layout == MXFP4_LAYOUT_TILED;
     if (dtype != MXFP4_IN_BF16 && dtype != MXFP4_IN_F32) return MXFP4_ERR_ARG;
     if (axis != 0 && axis != 1) return MXFP4_ERR_ARG;
-    if (hadamard != 0 && hadamard != 16 && hadamard != 32) return MXFP4_ERR_ARG;
+    if (!valid_rotation(hadamard)) return MXFP4_ERR_ARG;
     if (rounding != MXFP4_RNE && rounding != MXFP4_SR_PHILOX) return MXFP4_ERR_ARG;
     if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return MXFP4_ERR_SHAPE;
     const int64_t L = axis ? cols : rows;
@@ -134,7 +144,7 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
 {
     if (!cfg) return MXFP4_ERR_NULL;
     if (M < 0 || K < 0 || N < 0 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return MXFP4_ERR_SHAPE;
-    if (cfg->hadamard != 0 && cfg->hadamard != 16 && cfg->hadamard != 32) return MXFP4_ERR_ARG;
+    if (!valid_rotation(cfg->hadamard)) return MXFP4_ERR_ARG;
     if ((cfg->rnd_a != MXFP4_RNE && cfg->rnd_a != MXFP4_SR_PHILOX) ||
         (cfg->rnd_b != MXFP4_RNE && cfg->rnd_b != MXFP4_SR_PHILOX))
         return MXFP4_ERR_ARG;
@@ -148,7 +158,9 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     if (sp.out_rows == 0 || sp.out_cols == 0) return MXFP4_OK;
     if (!out) return MXFP4_ERR_NULL;
     if (!aligned(out, 4)) return MXFP4_ERR_ALIGN;
-    const float alpha = cfg->hadamard ? 1.0f / (float)cfg->hadamard : 1.0f;
+    // H H^T = h I, also with the randomized sign diagonal (D D^T = I)
+    const int h = cfg->hadamard & ~MXFP4_RHT;
+    const float alpha = h ? 1.0f / (float)h : 1.0f;
     if (sp.kc == 0) {
         // empty contraction: the product is all zeros
         if (mxfp4_status_t st = check_device()) return st;

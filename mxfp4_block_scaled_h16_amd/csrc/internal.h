@@ -6,6 +6,11 @@
 
 namespace mx {
 
+// hadamard argument of the launchers: the size (0, 16, 32) in the low byte, plus the
+// randomized-Hadamard flag (the public MXFP4_RHT).
+constexpr int kHadamardSize = 0xFF;
+constexpr int kRandomizedHadamard = 0x100;
+
 // Arguments are validated by the caller; these only pick a kernel and enqueue it.
 // tiled: write the tiled layout (L % 512 == 0; ldq and lds unused), else row-major.
 hipError_t launch_quantize_rows(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,

@@ -160,6 +160,27 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return r;
 }
 
+// ---------------------------------------------------------------- randomized Hadamard -------
+// Sign diagonal of the randomized rotation y = H (d .* x): bit t of the returned word is set iff
+// position 32 c + t along the quantized axis is negated. Word c % 4 of the Philox4x32-10 block
+// with counter (c / 4 mod 2^32, c / 4 >> 32, 0, 1): the last counter word 1 keeps these words
+// apart from the stochastic-rounding words (last counter word 0) under the same key.
+__device__ __forceinline__ uint32_t rht_sign_word(uint64_t c, uint32_t key0, uint32_t key1)
+{
+    const uint64_t b = c >> 2;
+    const Philox4 r = philox4x32_10((uint32_t)b, (uint32_t)(b >> 32), 0u, 1u, key0, key1);
+    const uint32_t w = (uint32_t)c & 3u;
+    return w == 0u ? r.w[0] : (w == 1u ? r.w[1] : (w == 2u ? r.w[2] : r.w[3]));
+}
+
+// Negate v[e] where bit e of `bits` is set (an exact sign-bit flip).
+template <int N>
+__device__ __forceinline__ void apply_signs(float *v, uint32_t bits)
+{
+#pragma unroll
+    for (int e = 0; e < N; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((bits >> e) & 1u) << 31));
+}
+
 // ---------------------------------------------------------------------------- stochastic -----
 // Stochastic codes of 8 consecutive values y[0..7] (not yet scaled) whose first element has
 // position index0 (a multiple of 8) in the quantized output: two Philox blocks, word k of

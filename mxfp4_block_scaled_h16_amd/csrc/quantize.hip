@@ -54,7 +54,7 @@ __device__ __forceinline__ int64_t tiled_scale(uint32_t o, uint32_t c, int64_t L
     return ((int64_t)(o / 64) * (L / 512) + c / 16) * 1024 + (o % 64) * 16 + (c % 16);
 }
 
-template <int H, bool F32, bool SR, bool TILED>
+template <int H, bool F32, bool SR, bool TILED, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t groups_per_row, uint32_t total_groups,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kRowsUnroll; ++u) {
+        if constexpr (RHT) apply_signs<8>(v[u], (rht_sign_word(grp[u] / 4, key0, key1) >> (8 * (grp[u] % 4))) & 0xFFu);
         if constexpr (H >= 16) {
             fwht_regs<8>(v[u]);
             fwht_cross_stage<1>(v[u], upper1);
@@ -147,7 +148,7 @@ constexpr int kColsTileRows = 256;
 constexpr int kColsRowBytes = 128;
 constexpr int kColsOutStride = 144;  // 128 bytes of codes + 16 of padding per output row
 
-template <int H, bool F32, bool SR, bool TILED>
+template <int H, bool F32, bool SR, bool TILED, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t rows, uint32_t cols, uint32_t col_tiles,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
@@ -211,9 +212,11 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
                     v[1][i] = bf16_hi(w);
                 }
             }
+            const uint32_t signs = RHT ? rht_sign_word(r0 / 32 + blk, key0, key1) : 0u;
 #pragma unroll
             for (int cc = 0; cc < kColsPerThread; ++cc) {
                 const uint32_t tc = cp * kColsPerThread + cc;  // tile column = quantized row
+                if constexpr (RHT) apply_signs<32>(v[cc], signs);
                 rotate_block<H>(v[cc]);
                 uint32_t amax = 0u;
 #pragma unroll
@@ -286,7 +289,7 @@ struct DualOut {
     uint32_t sr, tiled;
 };
 
-template <int H, bool F32>
+template <int H, bool F32, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t rows, uint32_t cols, uint32_t col_tiles,
     DualOut o1, DualOut o0)
@@ -329,6 +332,9 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
 #pragma unroll
             for (int p = 0; p < kParts; ++p) dst[p] = raw[k][p];
         }
+        // randomized rotation: this lane's 8 positions along the rows are the same for every k
+        const uint32_t g1 = c0 / 8 + gi;
+        const uint32_t row_signs = RHT ? (rht_sign_word(g1 / 4, o1.key0, o1.key1) >> (8 * (g1 % 4))) & 0xFFu : 0u;
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
             const uint32_t tr = 16 * k + 4 * wave + lane / 16;
@@ -346,6 +352,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
                     v[2 * u + 1] = bf16_hi(w[u]);
                 }
             }
+            if constexpr (RHT) apply_signs<8>(v, row_signs);
             if constexpr (H >= 16) {
                 fwht_regs<8>(v);
                 fwht_cross_stage<1>(v, upper1);
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
             amax = max(amax, quad_xor<1>(amax));
             amax = max(amax, quad_xor<2>(amax));
             const uint32_t sc = e8m0_from_amax_bits(amax);
-            const uint32_t o = r0 + tr, g = c0 / 8 + gi;   // quantized row, global group
+            const uint32_t o = r0 + tr, g = g1;   // quantized row, global group
             uint32_t word;
             if (o1.sr) {
                 word = encode8_stochastic(v, sc, (uint64_t)o * cols + 8u * g, o1.key0, o1.key1, o1.stream_id);
@@ -397,9 +404,11 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
             }
         }
         __syncthreads();
+        const uint32_t col_signs = RHT ? rht_sign_word(r0 / 32 + blk, o0.key0, o0.key1) : 0u;
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const uint32_t tc = F32 ? lane + 64 * cc : 2 * lane + cc;  // tile column = quantized row
+            if constexpr (RHT) apply_signs<32>(v[cc], col_signs);
             rotate_block<H>(v[cc]);
             uint32_t amax = 0u;
 #pragma unroll
@@ -460,17 +469,17 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
     }
 }
 
-template <int H, bool F32>
+template <int H, bool F32, bool RHT>
 hipError_t dual_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, const DualOut &o1,
                          const DualOut &o0, hipStream_t stream)
 {
     const int64_t col_tiles = (cols + kDualTile - 1) / kDualTile;
     const int64_t row_tiles = (rows + kDualTile - 1) / kDualTile;
-    return launch(quant_dual_kernel<H, F32>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0, stream,
+    return launch(quant_dual_kernel<H, F32, RHT>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0, stream,
                   x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles, o1, o0);
 }
 
-template <int H, bool F32, bool SR, bool TILED>
+template <int H, bool F32, bool SR, bool TILED, bool RHT>
 hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                          hipStream_t stream)
@@ -479,11 +488,11 @@ hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx,
     const uint32_t total = (uint32_t)(rows * (cols / 8));
     const uint32_t per_block = kThreads * kRowsUnroll;
     const dim3 grid((total + per_block - 1) / per_block);
-    return launch(quant_rows_kernel<H, F32, SR, TILED>, grid, dim3(kThreads), 0, stream, x, ldx, gpr, total, q,
+    return launch(quant_rows_kernel<H, F32, SR, TILED, RHT>, grid, dim3(kThreads), 0, stream, x, ldx, gpr, total, q,
                   ldq, scales, lds, (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, cols);
 }
 
-template <int H, bool F32, bool SR, bool TILED>
+template <int H, bool F32, bool SR, bool TILED, bool RHT>
 hipError_t cols_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                          hipStream_t stream)
@@ -491,7 +500,7 @@ hipError_t cols_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx,
     const int64_t tile_cols = kColsRowBytes / (F32 ? 4 : 2);
     const int64_t col_tiles = (cols + tile_cols - 1) / tile_cols;
     const int64_t row_tiles = (rows + kColsTileRows - 1) / kColsTileRows;
-    return launch(quant_cols_kernel<H, F32, SR, TILED>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0,
+    return launch(quant_cols_kernel<H, F32, SR, TILED, RHT>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0,
                   stream, x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles, q, ldq, scales, lds,
                   (uint32_t)seed, (uint32_t)(seed >> 32), stream_id);
 }
@@ -512,21 +521,28 @@ hipError_t pick(int h, bool f32, bool sr, A... a)
     return hipErrorInvalidValue;
 }
 
+// the randomized variants exist only for H = 16 and 32 (the entry points reject RHT with H = 0)
 template <int H, bool F32, bool SR>
 struct RowsSel {
     template <typename... A>
-    static hipError_t run(bool tiled, A... a)
+    static hipError_t run(bool tiled, bool rht, A... a)
     {
-        return tiled ? rows_dispatch<H, F32, SR, true>(a...) : rows_dispatch<H, F32, SR, false>(a...);
+        if constexpr (H > 0) {
+            if (rht) return tiled ? rows_dispatch<H, F32, SR, true, true>(a...) : rows_dispatch<H, F32, SR, false, true>(a...);
+        }
+        return tiled ? rows_dispatch<H, F32, SR, true, false>(a...) : rows_dispatch<H, F32, SR, false, false>(a...);
     }
 };
 
 template <int H, bool F32, bool SR>
 struct ColsSel {
     template <typename... A>
-    static hipError_t run(bool tiled, A... a)
+    static hipError_t run(bool tiled, bool rht, A... a)
     {
-        return tiled ? cols_dispatch<H, F32, SR, true>(a...) : cols_dispatch<H, F32, SR, false>(a...);
+        if constexpr (H > 0) {
+            if (rht) return tiled ? cols_dispatch<H, F32, SR, true, true>(a...) : cols_dispatch<H, F32, SR, false, true>(a...);
+        }
+        return tiled ? cols_dispatch<H, F32, SR, true, false>(a...) : cols_dispatch<H, F32, SR, false, false>(a...);
     }
 };
 
@@ -537,8 +553,8 @@ hipError_t launch_quantize_rows(const void *x, bool f32, int64_t rows, int64_t c
                                 bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream)
 {
-    return pick<RowsSel>(hadamard, f32, stochastic, tiled, x, rows, cols, ldx, seed, stream_id, q, ldq,
-                         scales, lds, stream);
+    return pick<RowsSel>(hadamard & kHadamardSize, f32, stochastic, tiled, (hadamard & kRandomizedHadamard) != 0,
+                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, stream);
 }
 
 hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
@@ -546,8 +562,8 @@ hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t c
                                 bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream)
 {
-    return pick<ColsSel>(hadamard, f32, stochastic, tiled, x, rows, cols, ldx, seed, stream_id, q, ldq,
-                         scales, lds, stream);
+    return pick<ColsSel>(hadamard & kHadamardSize, f32, stochastic, tiled, (hadamard & kRandomizedHadamard) != 0,
+                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, stream);
 }
 
 hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
@@ -559,13 +575,18 @@ hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t c
                        o.stochastic ? 1u : 0u, o.tiled ? 1u : 0u};
     };
     const DualOut o1 = conv(axis1), o0 = conv(axis0);
-    switch (hadamard * 2 + (f32 ? 1 : 0)) {
-    case 0: return dual_dispatch<0, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 1: return dual_dispatch<0, true>(x, rows, cols, ldx, o1, o0, stream);
-    case 32: return dual_dispatch<16, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 33: return dual_dispatch<16, true>(x, rows, cols, ldx, o1, o0, stream);
-    case 64: return dual_dispatch<32, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 65: return dual_dispatch<32, true>(x, rows, cols, ldx, o1, o0, stream);
+    const bool rht = (hadamard & kRandomizedHadamard) != 0;
+    switch ((hadamard & kHadamardSize) * 4 + (f32 ? 2 : 0) + (rht ? 1 : 0)) {
+    case 0: return dual_dispatch<0, false, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 2: return dual_dispatch<0, true, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 64: return dual_dispatch<16, false, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 65: return dual_dispatch<16, false, true>(x, rows, cols, ldx, o1, o0, stream);
+    case 66: return dual_dispatch<16, true, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 67: return dual_dispatch<16, true, true>(x, rows, cols, ldx, o1, o0, stream);
+    case 128: return dual_dispatch<32, false, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 129: return dual_dispatch<32, false, true>(x, rows, cols, ldx, o1, o0, stream);
+    case 130: return dual_dispatch<32, true, false>(x, rows, cols, ldx, o1, o0, stream);
+    case 131: return dual_dispatch<32, true, true>(x, rows, cols, ldx, o1, o0, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 3
+    assert L.mxfp4_abi_version() == 4
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -92,6 +92,9 @@ def test_quantize_argument_errors(L):
     assert _q(L, cols=48, ldx=48, ldq=24) == 2            # length not a multiple of 32
     assert _q(L, rows=-1) == 2
     assert _q(L, h=8) == 3                                  # hadamard size
+    assert _q(L, h=0x100) == 3                              # randomized flag needs a size
+    assert _q(L, h=0x110, x=None) == 1                      # 16 | MXFP4_RHT is a valid rotation
+    assert _q(L, h=0x300) == 3                              # unknown flag bit
     assert _q(L, axis=2) == 3
     assert _q(L, rnd=5) == 3
     assert _q(L, dtype=3) == 3

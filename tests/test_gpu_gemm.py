@@ -200,3 +200,30 @@ def test_gemm_split_k_with_workspace(M, N, K, layout):
     assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32)), "split-K result not deterministic"
     ref, basis = oracle.gemm(aq, as_, bq, bs, alpha=0.25, with_abs=True)
     assert_gemm_close(c1, ref, basis, TOL, "split-k gemm %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("kind", ["fprop", "dgrad", "wgrad"])
+@pytest.mark.parametrize("h", [16, 32])
+def test_linear_randomized_hadamard(kind, h):
+    """The three linear GEMMs with hadamard = h | MXFP4_RHT (both operands share the signs of the
+    call's seed), every output against the oracle; Wgrad with SR on both operands."""
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(80 + h)
+    M, K, N = 256, 512, 384
+    x = inputs.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = inputs.bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    dy = inputs.bf16_bits((rng.standard_t(3, (M, N)) * 1e-3).astype(np.float32))
+    hh = h | mx.RHT
+    seed = 0xFEED + h
+    announce("linear rht", kind, h)
+    if kind == "fprop":
+        got = host(mx.linear_fprop(bf16_dev(x), bf16_dev(w), hh, seed=seed))
+        ref, basis = oracle.linear_fprop(x, w, hadamard=h | oracle.RHT, seed=seed, with_abs=True)
+    elif kind == "dgrad":
+        got = host(mx.linear_dgrad(bf16_dev(dy), bf16_dev(w), hh, seed=seed))
+        ref, basis = oracle.linear_dgrad(dy, w, hadamard=h | oracle.RHT, seed=seed, with_abs=True)
+    else:
+        got = host(mx.linear_wgrad(bf16_dev(dy), bf16_dev(x), hh, "sr", "sr", seed))
+        ref, basis = oracle.linear_wgrad(dy, x, hadamard=h | oracle.RHT, rnd_a=oracle.SR, rnd_b=oracle.SR,
+                                         seed=seed, with_abs=True)
+    assert_gemm_close(got, ref, basis, TOL, "rht %s h%d" % (kind, h))

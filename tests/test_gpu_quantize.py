@@ -142,3 +142,33 @@ def test_tiled_layout_bit_exact(axis, h, rounding):
         rq, rs = oracle.quantize(x, axis=axis, hadamard=h, rounding=rounding, seed=9, stream=1)
         assert np.array_equal(sh, rs), "tiled scales differ"
         assert np.array_equal(qh, rq), "tiled codes differ"
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("h", [16, 32])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_randomized_hadamard_bit_exact(axis, h, rounding):
+    """hadamard = h | MXFP4_RHT: sign diagonal keyed by the seed before the rotation, both
+    layouts, ragged outer sizes."""
+    from tests.gpu_util import untile
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(70 + axis + h + rounding)
+    for outer, L, layout in ((96, 160, "rows"), (300, 512, "tiled"), (33, 1024, "rows"), (256, 1536, "tiled")):
+        if layout == "rows" and axis == 0 and outer % 8:
+            continue  # keep 16-byte row strides for the transposed case
+        shape = (outer, L) if axis == 1 else (L, outer)
+        x = inputs.bf16_bits(rng.standard_normal(shape).astype(np.float32) * 2)
+        seed = 0x1234567890ABCDEF + outer
+        announce("quantize rht", shape, "axis", axis, "h", h, "rnd", rounding, layout)
+        ld = -(-shape[1] // 8) * 8
+        padded = np.zeros((shape[0], ld), dtype=np.uint16)
+        padded[:, :shape[1]] = x
+        dev = bf16_dev(padded)[:, :shape[1]]
+        q, s = mx.quantize(dev, axis=axis, hadamard=h | mx.RHT, rounding=rounding, seed=seed, stream_id=1,
+                           layout=layout)
+        qh, sh = host(q), host(s)
+        if layout == "tiled":
+            qh, sh = untile(qh, sh, outer, L)
+        rq, rs = oracle.quantize(x, axis=axis, hadamard=h | oracle.RHT, rounding=rounding, seed=seed, stream=1)
+        assert np.array_equal(sh, rs), "rht scales differ"
+        assert np.array_equal(qh, rq), "rht codes differ"

@@ -132,3 +132,16 @@ def test_dual_full_size_qkv():
     check_dual(x, 16, 0, 1, seed0=0x5EED, stream0=1, lay1="tiled", lay0="tiled", what="QKV X 8192x4096")
     check_dual(dy, 16, 0, 1, seed0=0x5EED, stream0=0, lay1="tiled", lay0="tiled", what="QKV dY 8192x6144")
     check_dual(w, 16, 0, 0, lay1="tiled", lay0="tiled", what="QKV W 6144x4096")
+
+
+@pytest.mark.parametrize("h", [16, 32])
+def test_dual_randomized_hadamard(h):
+    """Both outputs with the randomized rotation (each output's signs keyed by its own seed,
+    indexed along its own quantized axis), rows and tiled layouts, nearest and SR."""
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(700 + h)
+    for rows, cols, lay1, lay0, r1, r0 in ((160, 96, "rows", "rows", 0, 1), (512, 1024, "tiled", "tiled", 0, 1),
+                                           (288, 512, "tiled", "rows", 1, 0)):
+        x = inputs.bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32) * 2)
+        check_dual(x, h | mx.RHT, r1, r0, seed1=41, seed0=42, stream1=0, stream0=1, lay1=lay1, lay0=lay0,
+                   what="rht")
