@@ -59,6 +59,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--settle", type=float, default=1.0,
                    help="seconds of untimed steps before the warm-up (GPU clock ramp)")
+    p.add_argument("--no-library-baselines", action="store_true",
+                   help="skip the vendor GEMM baselines (hipBLASLt MXFP8 / MXFP4 / FP8 / bf16)")
     p.add_argument("--separate-quant", action="store_true",
                    help="one quantizer launch per axis instead of one dual launch per tensor")
     p.add_argument("--copy-calibration", action="store_true",
@@ -406,6 +408,51 @@ def run_timed(plan, steps, warmup):
     return (t1 - t0) * 1e3 / steps, per_launch.mean(0)
 
 
+def library_baselines(M, N, K, steps, settle_s=0.25):
+    """Vendor GEMMs (hipBLASLt through torch._scaled_mm / torch.mm) at one product shape, as
+    context: block-scaled MXFP8 and MXFP4 (E8M0 scale per 32 along K), per-tensor FP8 and
+    bf16. The block-scaled paths accept only bf16/fp16 outputs, so they write half the output
+    bytes this library's FP32 GEMM writes. Operands are random codes with scales near 1.
+    Each is settled for `settle_s` seconds, then timed over K launches (host clock)."""
+    import torch
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(0)
+    e8 = lambda rows: torch.randint(124, 131, (rows, K // 32), dtype=torch.uint8, device=dev,  # noqa: E731
+                                    generator=g).view(torch.float8_e8m0fnu)
+    a8 = torch.randn(M, K, device=dev, generator=g).to(torch.float8_e4m3fn)
+    b8 = torch.randn(N, K, device=dev, generator=g).to(torch.float8_e4m3fn)
+    a4 = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=g).view(torch.float4_e2m1fn_x2)
+    b4 = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g).view(torch.float4_e2m1fn_x2)
+    sa, sb = e8(M), e8(N)
+    one = torch.tensor(1.0, device=dev)
+    abf = torch.randn(M, K, device=dev, generator=g, dtype=torch.bfloat16)
+    bbf = torch.randn(N, K, device=dev, generator=g, dtype=torch.bfloat16)
+    cases = {
+        "hipblaslt_mxfp8_e4m3": lambda: torch._scaled_mm(a8, b8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
+        "hipblaslt_mxfp4": lambda: torch._scaled_mm(a4, b4.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
+        "hipblaslt_fp8_e4m3_per_tensor": lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,
+                                                                  out_dtype=torch.bfloat16),
+        "hipblaslt_bf16": lambda: torch.mm(abf, bbf.t()),
+    }
+    out = {"shape": "M=%d N=%d K=%d" % (M, N, K), "output": "bf16"}
+    for name, f in cases.items():
+        try:
+            t_end = time.perf_counter() + settle_s
+            while time.perf_counter() < t_end:
+                f()
+                torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                f()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / steps
+            out[name] = {"us": round(us, 2), "tflops": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1)}
+        except Exception as e:  # a baseline the runtime does not offer is reported, not fatal
+            out[name] = {"error": str(e)[:200]}
+    return out
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -479,6 +526,14 @@ def main():
                  "launches": [label for label, _, _, _ in fplan.op_list]}
         del fplan
 
+    baselines = None
+    if args.workload == "qkv" and not args.no_library_baselines:
+        baselines = library_baselines(M, projs[0][2], projs[0][1], args.steps)
+        gemm_f = next(t for (label, kind, _, _), t in zip(plan.op_list, avg_ms) if label.startswith("gemm Fprop"))
+        baselines["this_library_mxfp4_fp32_output"] = {"us": round(float(gemm_f) * 1e3, 2),
+                                                       "tflops": round(2.0 * M * projs[0][2] * projs[0][1]
+                                                                       / (float(gemm_f) * 1e-3) / 1e12, 1)}
+
     if args.copy_calibration:
         buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         buf2 = torch.empty_like(buf)
@@ -504,6 +559,8 @@ def main():
     }
     if fprop is not None:
         line["fprop_only"] = fprop
+    if baselines is not None:
+        line["library_baselines"] = baselines
     print(json.dumps(line), flush=True)
     return 0
 
