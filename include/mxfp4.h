@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 4
+#define MXFP4_ABI_VERSION 5
 
 typedef enum {
     MXFP4_OK = 0,
@@ -180,6 +180,29 @@ mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
                           int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,
                           mxfp4_layout_t layout, void *workspace, size_t ws_bytes, void *stream);
+
+/* Output element type of mxfp4_gemm_ex. */
+typedef enum { MXFP4_OUT_F32 = 0, MXFP4_OUT_BF16 = 1 } mxfp4_out_dtype_t;
+
+/*
+ * mxfp4_gemm_ex -- mxfp4_gemm with an epilogue: c = alpha * A B^T + beta * c.
+ *
+ * Defined by: the same product as mxfp4_gemm (Methodology section). The extra terms serve the
+ * training step around it: beta = 1 accumulates a weight gradient into an existing FP32 buffer
+ * (gradient accumulation over micro-batches), and a bf16 output halves the bytes of an
+ * activation-sized result.
+ *   c        device, c_dtype[M][ldc]: MXFP4_OUT_F32 (4-byte aligned) or MXFP4_OUT_BF16 (2-byte
+ *            aligned; the FP32 result is rounded to nearest even once, after beta * c is added).
+ *   beta     c is read only when beta != 0 (it may then hold anything, even NaN, when beta == 0).
+ * The sum alpha * acc + beta * c is formed in binary32 (two roundings). Other arguments,
+ * requirements and the workspace are those of mxfp4_gemm; with beta == 0 and FP32 output it runs
+ * the same kernels as mxfp4_gemm.
+ */
+mxfp4_status_t mxfp4_gemm_ex(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
+                             const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
+                             int64_t M, int64_t N, int64_t K, float alpha, float beta, void *c,
+                             mxfp4_out_dtype_t c_dtype, int64_t ldc, mxfp4_layout_t layout,
+                             void *workspace, size_t ws_bytes, void *stream);
 
 /* Workspace bytes that let mxfp4_gemm split the contraction of an M x N x K product (0 when the
  * product is not split; also 0 for invalid sizes). */

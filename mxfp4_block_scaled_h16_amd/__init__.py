@@ -71,6 +71,9 @@ def lib():
     L.mxfp4_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, vp, i64,
                              ci, vp, ctypes.c_size_t, vp]
     L.mxfp4_gemm.restype = ci
+    L.mxfp4_gemm_ex.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float,
+                                vp, ci, i64, ci, vp, ctypes.c_size_t, vp]
+    L.mxfp4_gemm_ex.restype = ci
     L.mxfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.mxfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
     L.mxfp4_tiled_sizes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
@@ -211,12 +214,13 @@ def gemm_workspace_bytes(M, N, K) -> int:
 
 
 def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None, layout="rows", m=None, n=None,
-         workspace=None):
-    """c[m][n] = alpha * sum_k deq(A)[m][k] deq(B)[n][k] (FP32 [M, N]).
+         workspace=None, beta=0.0, out_dtype=None):
+    """c[m][n] = alpha * sum_k deq(A)[m][k] deq(B)[n][k] + beta * c[m][n] (FP32 or bf16 [M, N]).
 
     Tiled operands are padded to 256 rows, so M and N come from `out`, or `m` and `n`. A device
     workspace of gemm_workspace_bytes(M, N, K) bytes lets few-tile products split K; "auto"
-    allocates it."""
+    allocates it. beta != 0 reads `out` (mxfp4_gemm_ex); a bf16 `out` (or out_dtype) gets the
+    result rounded to nearest even."""
     lay = _layout(layout)
     for t, nm in ((aq, "aq"), (as_, "as"), (bq, "bq"), (bs, "bs")):
         _require_cuda(t, nm)
@@ -227,16 +231,27 @@ def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None, layout="rows", m=Non
     M = M if m is None else int(m)
     N = N if n is None else int(n)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=aq.device)
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing `out`")
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=aq.device)
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(-1) != 1:
+        raise TypeError("out must be float32 or bfloat16 with unit column stride")
     if isinstance(workspace, str) and workspace == "auto":
         need = gemm_workspace_bytes(M, N, K)
         workspace = torch.empty(need, dtype=torch.uint8, device=aq.device) if need else None
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().mxfp4_gemm(aq.data_ptr(), aq.stride(0), as_.data_ptr(), as_.stride(0), bq.data_ptr(),
-                          bq.stride(0), bs.data_ptr(), bs.stride(0), M, N, K, float(alpha),
-                          out.data_ptr(), out.stride(0), lay, ws_ptr, ws_len, _stream(stream))
-    _check(st, "mxfp4_gemm")
+    if out.dtype == torch.float32 and beta == 0.0:
+        st = lib().mxfp4_gemm(aq.data_ptr(), aq.stride(0), as_.data_ptr(), as_.stride(0), bq.data_ptr(),
+                              bq.stride(0), bs.data_ptr(), bs.stride(0), M, N, K, float(alpha),
+                              out.data_ptr(), out.stride(0), lay, ws_ptr, ws_len, _stream(stream))
+        _check(st, "mxfp4_gemm")
+    else:
+        st = lib().mxfp4_gemm_ex(aq.data_ptr(), aq.stride(0), as_.data_ptr(), as_.stride(0), bq.data_ptr(),
+                                 bq.stride(0), bs.data_ptr(), bs.stride(0), M, N, K, float(alpha),
+                                 float(beta), out.data_ptr(), 1 if out.dtype == torch.bfloat16 else 0,
+                                 out.stride(0), lay, ws_ptr, ws_len, _stream(stream))
+        _check(st, "mxfp4_gemm_ex")
     return out
 
 

@@ -77,8 +77,8 @@ int64_t pad256(int64_t v) { return (v + 255) / 256 * 256; }
 
 mxfp4_status_t check_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
-                          int64_t M, int64_t N, int64_t K, const float *c, int64_t ldc,
-                          mxfp4_layout_t layout)
+                          int64_t M, int64_t N, int64_t K, const void *c, int64_t ldc,
+                          mxfp4_layout_t layout, size_t c_elem = 4)
 {
     if (layout != MXFP4_LAYOUT_ROWS && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_ARG;
     const bool tiled = layout == MXFP4_LAYOUT_TILED;
@@ -95,7 +95,7 @@ mxfp4_status_t check_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int
     if (!aligned(aq, 16) || !aligned(bq, 16)) return MXFP4_ERR_ALIGN;
     if (tiled ? (!aligned(as, 16) || !aligned(bs, 16)) : (lda % 16 != 0 || ldb % 16 != 0))
         return MXFP4_ERR_ALIGN;
-    if (!aligned(c, 4)) return MXFP4_ERR_ALIGN;
+    if (!aligned(c, c_elem)) return MXFP4_ERR_ALIGN;
     return MXFP4_OK;
 }
 
@@ -164,8 +164,8 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     if (sp.kc == 0) {
         // empty contraction: the product is all zeros
         if (mxfp4_status_t st = check_device()) return st;
-        return from_hip(mx::launch_fill_zero(out, sp.out_rows, sp.out_cols, sp.out_cols,
-                                             (hipStream_t)stream));
+        return from_hip(mx::launch_empty_product(out, false, sp.out_rows, sp.out_cols, sp.out_cols, 0.0f,
+                                                 (hipStream_t)stream));
     }
     if (!sp.a_src || !sp.b_src) return MXFP4_ERR_NULL;
     if (!aligned(sp.a_src, 16) || !aligned(sp.b_src, 16)) return MXFP4_ERR_ALIGN;
@@ -195,8 +195,8 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     if (e == hipSuccess) e = quant(sp.b_src, sp.b_rows, sp.b_cols, sp.b_axis, cfg->rnd_b, 1u, bq, bs, b.L);
     if (e == hipSuccess)
         e = mx::launch_gemm(aq, a.L / 2, as, a.L / 32, bq, b.L / 2, bs, b.L / 32, sp.out_rows,
-                            sp.out_cols, sp.kc, alpha, out, sp.out_cols, tiled, p + layout_bytes(a, b),
-                            ws_bytes - layout_bytes(a, b), s);
+                            sp.out_cols, sp.kc, alpha, 0.0f, out, false, sp.out_cols, tiled,
+                            p + layout_bytes(a, b), ws_bytes - layout_bytes(a, b), s);
     return from_hip(e);
 }
 
@@ -255,9 +255,26 @@ mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int
     if ((st = check_device()) != MXFP4_OK) return st;
     if (K == 0) {
         // empty contraction: the product is all zeros
-        return from_hip(mx::launch_fill_zero(c, M, N, ldc, (hipStream_t)stream));
+        return from_hip(mx::launch_empty_product(c, false, M, N, ldc, 0.0f, (hipStream_t)stream));
     }
-    return from_hip(mx::launch_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, alpha, c, ldc,
+    return from_hip(mx::launch_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, alpha, 0.0f, c, false, ldc,
+                                    layout == MXFP4_LAYOUT_TILED, workspace, ws_bytes,
+                                    (hipStream_t)stream));
+}
+
+mxfp4_status_t mxfp4_gemm_ex(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
+                             const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
+                             int64_t M, int64_t N, int64_t K, float alpha, float beta, void *c,
+                             mxfp4_out_dtype_t c_dtype, int64_t ldc, mxfp4_layout_t layout,
+                             void *workspace, size_t ws_bytes, void *stream)
+{
+    if (c_dtype != MXFP4_OUT_F32 && c_dtype != MXFP4_OUT_BF16) return MXFP4_ERR_ARG;
+    const bool bf16 = c_dtype == MXFP4_OUT_BF16;
+    mxfp4_status_t st = check_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, c, ldc, layout, bf16 ? 2 : 4);
+    if (st != MXFP4_OK || M == 0 || N == 0) return st;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    if (K == 0) return from_hip(mx::launch_empty_product(c, bf16, M, N, ldc, beta, (hipStream_t)stream));
+    return from_hip(mx::launch_gemm(aq, lda, as, ldas, bq, ldb, bs, ldbs, M, N, K, alpha, beta, c, bf16, ldc,
                                     layout == MXFP4_LAYOUT_TILED, workspace, ws_bytes,
                                     (hipStream_t)stream));
 }

@@ -23,6 +23,90 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kFmtFp4 = 4;  // format selector of the f8f6f4 MFMA family for E2M1
 
+// ---------------------------------------------------------------------------- output ---------
+// The general epilogue: c = alpha * (A B^T) + beta * c, stored as FP32 or bf16 (the FP32 value
+// rounded to nearest even by the hardware conversion). c is read only when beta != 0 (it may be
+// uninitialised otherwise).
+struct OutSpec {
+    void *c;
+    int64_t ldc;
+    float alpha, beta;
+    int bf16;
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// one output element (v = alpha * acc already)
+template <bool BF16>
+__device__ __forceinline__ void store1(const OutSpec &o, int64_t m, int64_t n, float v)
+{
+    if constexpr (BF16) {
+        uint16_t *p = static_cast<uint16_t *>(o.c) + m * o.ldc + n;
+        if (o.beta != 0.0f) v = v + o.beta * bf16_bits_to_float(*p);
+        *p = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    } else {
+        float *p = static_cast<float *>(o.c) + m * o.ldc + n;
+        if (o.beta != 0.0f) v = v + o.beta * *p;
+        *p = v;
+    }
+}
+
+__device__ __forceinline__ void store1_any(const OutSpec &o, int64_t m, int64_t n, float v)
+{
+    if (o.bf16)
+        store1<true>(o, m, n, v);
+    else
+        store1<false>(o, m, n, v);
+}
+
+// four consecutive outputs (v = alpha * acc already); vec: the row segment is aligned for one
+// 16-byte (FP32) or 8-byte (bf16) access and lies inside [0, N)
+template <bool BF16>
+__device__ __forceinline__ void store4(const OutSpec &o, int64_t m, int64_t n, int64_t N, f32x4v v, bool vec)
+{
+    if (!vec) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < N) store1<BF16>(o, m, n + e, v[e]);
+        return;
+    }
+    if constexpr (BF16) {
+        uint2 *p = reinterpret_cast<uint2 *>(static_cast<uint16_t *>(o.c) + m * o.ldc + n);
+        if (o.beta != 0.0f) {
+            const uint2 old = *p;
+            v[0] = v[0] + o.beta * bf16_bits_to_float(old.x & 0xFFFFu);
+            v[1] = v[1] + o.beta * bf16_bits_to_float(old.x >> 16);
+            v[2] = v[2] + o.beta * bf16_bits_to_float(old.y & 0xFFFFu);
+            v[3] = v[3] + o.beta * bf16_bits_to_float(old.y >> 16);
+        }
+        *p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    } else {
+        f32x4v *p = reinterpret_cast<f32x4v *>(static_cast<float *>(o.c) + m * o.ldc + n);
+        if (o.beta != 0.0f) v = v + o.beta * *p;
+        *p = v;
+    }
+}
+
+// the row segments of c starting at column n (a multiple of 4) allow vector accesses
+template <bool BF16>
+__device__ __forceinline__ bool out_vector_ok(const OutSpec &o)
+{
+    return (o.ldc % 4) == 0 && ((uintptr_t)o.c % (BF16 ? 8 : 16)) == 0;
+}
+
+// epilogue variants of the pipelined kernel
+constexpr int kEpiF32 = 0;      // c = alpha * A B^T, FP32 (nothing else compiled in)
+constexpr int kEpiF32Beta = 1;  // FP32 with beta
+constexpr int kEpiBF16 = 2;     // bf16 with beta
+
 // Workgroup tile 128 x 128, four wavefronts in a 2 x 2 arrangement, each 64 x 64 (2 x 2 MFMA
 // tiles of 32 x 32); one K step = 64 (two MX blocks per row).
 constexpr int kTileM = 128, kTileN = 128, kWaveM = 64, kWaveN = 64;
@@ -30,7 +114,7 @@ constexpr int kTileM = 128, kTileN = 128, kWaveM = 64, kWaveN = 64;
 __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
-    int M, int N, int K, float alpha, float *__restrict__ c, int64_t ldc)
+    int M, int N, int K, OutSpec out)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -95,7 +179,7 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int m = m_base + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
-                if (m < M) c[(int64_t)m * ldc + n] = alpha * acc[i][j][e];
+                if (m < M) store1_any(out, m, n, out.alpha * acc[i][j][e]);
             }
         }
 }
@@ -172,12 +256,13 @@ struct Geo {
     static constexpr int kDmaPerScales = 8 / NW;                    // per wavefront and group
 };
 
-template <int NW, bool TILED>
+// EPI: kEpiF32 writes FP32 c = alpha * A B^T (out.c a float pointer; no other epilogue code is
+// compiled in), kEpiF32Beta adds beta * c, kEpiBF16 writes bf16 (with beta * c).
+template <int NW, bool TILED, int EPI>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
-    int M, int N, int K, float alpha, float *__restrict__ c, int64_t ldc, int tiles_m, int tiles_n,
-    int splits, float *__restrict__ partials)
+    int M, int N, int K, OutSpec out, int tiles_m, int tiles_n, int splits, float *__restrict__ partials)
 {
     using G = Geo<NW>;
     constexpr int FI = G::FI, FJ = G::FJ;
@@ -420,13 +505,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
 
     // epilogue: acc[i][j] register q * 4 + t of lane (r, half) is
     // C[m0 + 128 wm + 32 i + r][n0 + kWaveCols wn + 32 j + 8 q + 4 half + t]. With split-K the
-    // unscaled partial product goes to partials[split][M][N] instead.
-    if (splits > 1) {
-        c = partials + (int64_t)split * M * N;
-        ldc = N;
-        alpha = 1.0f;
-    }
-    const bool full_cols = n0 + kBN <= N && (ldc % 4) == 0 && ((uintptr_t)c % 16) == 0;
+    // unscaled partial product goes to partials[split][M][N] (FP32, beta 0) instead.
+    if (splits > 1) out = OutSpec{partials + (int64_t)split * M * N, N, 1.0f, 0.0f, 0};
+    float *c = static_cast<float *>(out.c);
+    const int64_t ldc = out.ldc;
+    const float alpha = out.alpha;
+    // split-K partials are FP32 whatever the variant: a bf16 variant decides per launch
+    const bool bf16_now = EPI == kEpiBF16 && out.bf16;
+    const bool full_cols = n0 + kBN <= N && (bf16_now ? out_vector_ok<true>(out) : out_vector_ok<false>(out));
     if (full_cols) {
         // stage each 32-row slice of this wavefront's 128 x kWaveCols result through LDS so that
         // a store instruction writes whole rows (two rows of kWaveCols floats)
@@ -448,15 +534,32 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
                                       acc[i][jj][4 * q + 3]};
                     *reinterpret_cast<f32x4v *>(epi + r * kEpiRow + (32 * jj + 8 * q + 4 * half) * 4) = v;
                 }
+            constexpr int kStores = 32 / kRowsPerStore;
+            const int cc = 4 * (lane % kLanesPerRow);
+            const int64_t ncol = n0 + wn * G::kWaveCols + cc;
+            if constexpr (EPI == kEpiF32) {
 #pragma unroll
-            for (int p = 0; p < 32 / kRowsPerStore; ++p) {
-                const int rr = kRowsPerStore * p + lane / kLanesPerRow;
-                const int cc = 4 * (lane % kLanesPerRow);
-                f32x4v v = *reinterpret_cast<const f32x4v *>(epi + rr * kEpiRow + cc * 4);
-                v = v * alpha;
-                const int m = m0 + wm * 128 + 32 * i + rr;
-                if (m < M)
-                    *reinterpret_cast<f32x4v *>(c + (int64_t)m * ldc + n0 + wn * G::kWaveCols + cc) = v;
+                for (int p = 0; p < kStores; ++p) {
+                    const int rr = kRowsPerStore * p + lane / kLanesPerRow;
+                    f32x4v v = *reinterpret_cast<const f32x4v *>(epi + rr * kEpiRow + cc * 4);
+                    v = v * alpha;
+                    const int m = m0 + wm * 128 + 32 * i + rr;
+                    if (m < M) *reinterpret_cast<f32x4v *>(c + (int64_t)m * ldc + ncol) = v;
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < kStores; ++p) {
+                    const int rr = kRowsPerStore * p + lane / kLanesPerRow;
+                    f32x4v v = *reinterpret_cast<const f32x4v *>(epi + rr * kEpiRow + cc * 4);
+                    v = v * alpha;
+                    const int m = m0 + wm * 128 + 32 * i + rr;
+                    if (m < M) {
+                        if (bf16_now)
+                            store4<true>(out, m, ncol, N, v, true);
+                        else
+                            store4<false>(out, m, ncol, N, v, true);
+                    }
+                }
             }
         }
         return;
@@ -473,7 +576,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
                 const int n = n0 + wn * G::kWaveCols + 32 * jj + 8 * q + 4 * half;
                 const f32x4v v = {alpha * acc[i][jj][4 * q + 0], alpha * acc[i][jj][4 * q + 1],
                                   alpha * acc[i][jj][4 * q + 2], alpha * acc[i][jj][4 * q + 3]};
-                if (full_cols) {
+                if constexpr (EPI == kEpiBF16) {
+                    if (bf16_now)
+                        store4<true>(out, m, n, N, v, false);
+                    else
+                        store4<false>(out, m, n, N, v, false);
+                } else if constexpr (EPI == kEpiF32Beta) {
+                    store4<false>(out, m, n, N, v, false);
+                } else if (full_cols) {
                     *reinterpret_cast<f32x4v *>(crow + n) = v;
                 } else {
 #pragma unroll
@@ -484,34 +594,35 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ c, int64_t M, int64_t N,
-                                                       int64_t ldc)
+// an empty contraction: c = beta * c (c = 0 when beta is 0, without reading c)
+__global__ __launch_bounds__(256) void empty_product_kernel(OutSpec out, int64_t M, int64_t N)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < M * N) c[(i / N) * ldc + (i % N)] = 0.0f;
+    if (i < M * N) store1_any(out, i / N, i % N, 0.0f);
 }
 
-// c[m][n] = alpha * (p_0[m][n] + p_1[m][n] + ... + p_{S-1}[m][n]), summed in that fixed order
+// c[m][n] = alpha * (p_0[m][n] + p_1[m][n] + ... + p_{S-1}[m][n]) (+ beta * c), summed in that
+// fixed order
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ p, int splits, int64_t M,
-                                                            int64_t N, float alpha, float *__restrict__ c,
-                                                            int64_t ldc)
+                                                            int64_t N, OutSpec out)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= M * N) return;
     const int64_t mn = M * N;
     float acc = p[i];
     for (int s = 1; s < splits; ++s) acc += p[(int64_t)s * mn + i];
-    c[(i / N) * ldc + (i % N)] = alpha * acc;
+    store1_any(out, i / N, i % N, out.alpha * acc);
 }
 
 }  // namespace
 
-hipError_t launch_fill_zero(float *c, int64_t M, int64_t N, int64_t ldc, hipStream_t stream)
+hipError_t launch_empty_product(void *c, bool bf16, int64_t M, int64_t N, int64_t ldc, float beta,
+                                hipStream_t stream)
 {
     const int64_t total = M * N;
     if (total == 0) return hipSuccess;
-    return launch(fill_zero_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, c, M,
-                  N, ldc);
+    return launch(empty_product_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                  OutSpec{c, ldc, 0.0f, beta, bf16 ? 1 : 0}, M, N);
 }
 
 int gemm_splits(int64_t M, int64_t N, int64_t K)
@@ -535,9 +646,11 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 
 hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                        const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs, int64_t M,
-                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, bool tiled,
-                       void *workspace, size_t ws_bytes, hipStream_t stream)
+                       int64_t N, int64_t K, float alpha, float beta, void *c, bool bf16, int64_t ldc,
+                       bool tiled, void *workspace, size_t ws_bytes, hipStream_t stream)
 {
+    const OutSpec out{c, ldc, alpha, beta, bf16 ? 1 : 0};
+    const int epi = bf16 ? kEpiBF16 : (beta != 0.0f ? kEpiF32Beta : kEpiF32);
     const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
     const bool scales_aligned = ((uintptr_t)as % 16 == 0) && ((uintptr_t)bs % 16 == 0) &&
                                 ldas % 16 == 0 && ldbs % 16 == 0;
@@ -547,7 +660,7 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
     if (!pipelined) {
         const dim3 sgrid((unsigned)((N + kTileN - 1) / kTileN), (unsigned)((M + kTileM - 1) / kTileM));
         return launch(gemm_mxfp4_simple, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
-                      (int)M, (int)N, (int)K, alpha, c, ldc);
+                      (int)M, (int)N, (int)K, out);
     }
     int splits = gemm_splits(M, N, K);
     if (splits > 1 && (workspace == nullptr || ws_bytes < gemm_workspace_bytes(M, N, K) ||
@@ -555,15 +668,23 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
         splits = 1;
     float *partials = splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const dim3 grid((unsigned)(tiles_m * tiles_n * splits)), block(64 * kGemmWaves);
-    hipError_t e = tiled
-        ? launch(gemm_mxfp4_pipelined<kGemmWaves, true>, grid, block, 0, stream, aq, lda, as, ldas, bq, ldb,
-                 bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m, tiles_n, splits, partials)
-        : launch(gemm_mxfp4_pipelined<kGemmWaves, false>, grid, block, 0, stream, aq, lda, as, ldas, bq, ldb,
-                 bs, ldbs, (int)M, (int)N, (int)K, alpha, c, ldc, tiles_m, tiles_n, splits, partials);
+    const auto run = [&](auto kernel) {
+        return launch(kernel, grid, block, 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs, (int)M, (int)N, (int)K,
+                      out, tiles_m, tiles_n, splits, partials);
+    };
+    hipError_t e;
+    if (tiled)
+        e = epi == kEpiBF16 ? run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiBF16>)
+          : epi == kEpiF32Beta ? run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32Beta>)
+                               : run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32>);
+    else
+        e = epi == kEpiBF16 ? run(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiBF16>)
+          : epi == kEpiF32Beta ? run(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiF32Beta>)
+                               : run(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiF32>);
     if (e != hipSuccess || splits == 1) return e;
     const int64_t total = M * N;
     return launch(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                  (const float *)partials, splits, M, N, alpha, c, ldc);
+                  (const float *)partials, splits, M, N, out);
 }
 
 }  // namespace mx

@@ -46,15 +46,19 @@ hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t c
 // otherwise row-major with leading dimensions. A workspace of gemm_workspace_bytes() bytes
 // (16-byte aligned) lets a GEMM with few output tiles split K (gemm_splits() ways) into FP32
 // partials that a second kernel sums in fixed order; without it the GEMM runs unsplit.
+// c = alpha * A B^T + beta * c, FP32 (bf16 = false) or bf16 (round to nearest even); c is not
+// read when beta == 0. beta == 0 with FP32 output runs the FP32-only kernel instantiation.
 hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                        const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs, int64_t M,
-                       int64_t N, int64_t K, float alpha, float *c, int64_t ldc, bool tiled,
-                       void *workspace, size_t ws_bytes, hipStream_t stream);
+                       int64_t N, int64_t K, float alpha, float beta, void *c, bool bf16, int64_t ldc,
+                       bool tiled, void *workspace, size_t ws_bytes, hipStream_t stream);
 int gemm_splits(int64_t M, int64_t N, int64_t K);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // c[m][n] = 0 for m < M, n < N (a kernel, not a memset, so it is safe inside captured graphs).
-hipError_t launch_fill_zero(float *c, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);
+// K == 0: c = beta * c (zeros when beta == 0, c not read)
+hipError_t launch_empty_product(void *c, bool bf16, int64_t M, int64_t N, int64_t ldc, float beta,
+                                hipStream_t stream);
 
 // Launch a kernel through hipLaunchKernel so the runtime's error comes back directly.
 template <typename... Params, typename... Args>

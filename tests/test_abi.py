@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 4
+    assert L.mxfp4_abi_version() == 5
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -185,3 +185,15 @@ def test_linear_workspace_uses_tiled_padding(L):
     assert mx.workspace_bytes(mx.FPROP, M, K, N) == want
     # contraction 96 (not a multiple of 512): row-major, no padding
     assert mx.workspace_bytes(mx.FPROP, 64, 96, 32) == r(64 * 48) + r(64 * 3) + r(32 * 48) + r(32 * 3)
+
+
+def test_gemm_ex_argument_errors(L):
+    def g(c=1 << 12, dtype=0, M=64, N=64, K=64, ldc=64, beta=0.0):
+        return L.mxfp4_gemm_ex(1 << 12, 32, 1 << 12, 2, 1 << 12, 32, 1 << 12, 2, M, N, K, 1.0, beta, c, dtype,
+                               ldc, 0, None, 0, None)
+    assert g(dtype=2) == 3                    # output type
+    assert g(c=(1 << 12) + 1, dtype=1) == 4   # bf16 output needs 2-byte alignment
+    assert g(c=(1 << 12) + 2, dtype=0) == 4   # FP32 output needs 4-byte alignment
+    assert g(c=None) == 1
+    assert g(ldc=32) == 3                     # ldc < N
+    assert g(M=0) == 0 and g(M=0, c=None) == 0

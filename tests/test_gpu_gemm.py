@@ -227,3 +227,70 @@ def test_linear_randomized_hadamard(kind, h):
         ref, basis = oracle.linear_wgrad(dy, x, hadamard=h | oracle.RHT, rnd_a=oracle.SR, rnd_b=oracle.SR,
                                          seed=seed, with_abs=True)
     assert_gemm_close(got, ref, basis, TOL, "rht %s h%d" % (kind, h))
+
+
+def _bf16_to_f64(t_u16):
+    return (np.asarray(t_u16, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("M,N,K,layout,ws", [
+    (512, 768, 1024, "tiled", False),    # pipelined, whole tiles (LDS-staged epilogue)
+    (300, 520, 1024, "tiled", False),    # ragged edges (direct epilogue)
+    (512, 4096, 8192, "tiled", True),    # split-K partials + reduce kernel
+    (200, 72, 96, "rows", False),        # K % 512 != 0: the plain kernel
+    (64, 96, 0, "rows", False),          # empty contraction: c = beta * c
+])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("beta", [0.0, 1.0, -0.5])
+def test_gemm_ex_epilogue(M, N, K, layout, ws, out_dtype, beta):
+    """c = alpha A B^T + beta c in FP32 or bf16, on every kernel path. Bar: the GEMM tolerance on
+    alpha * sum|ab| + |beta c|, plus (bf16) the half-ulp rounding of the result, 2^-8 |c|."""
+    from tests.gpu_util import tile
+    import mxfp4_block_scaled_h16_amd as mx
+    import torch
+    rng = np.random.default_rng(M + 7 * N + K + int(4 * beta) + (3 if out_dtype == "bf16" else 0))
+    Kq = max(K, 32)
+    aq, as_ = random_operand(rng, M, Kq)
+    bq, bs = random_operand(rng, N, Kq)
+    if layout == "tiled":
+        ra, rb = -(-M // 256) * 256, -(-N // 256) * 256
+        da = [_dev_u8(t.reshape(ra, -1)) for t in tile(aq, as_, M, K)]
+        db = [_dev_u8(t.reshape(rb, -1)) for t in tile(bq, bs, N, K)]
+    else:
+        da, db = [_dev_u8(aq[:, :K // 2]), _dev_u8(as_[:, :K // 32])], [_dev_u8(bq[:, :K // 2]), _dev_u8(bs[:, :K // 32])]
+    c_in = (rng.standard_normal((M, N)) * 50).astype(np.float32)
+    if out_dtype == "bf16":
+        c_bits = inputs.bf16_bits(c_in)
+        out = torch.from_numpy(c_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        c_in64 = _bf16_to_f64(c_bits)
+    else:
+        out = torch.from_numpy(c_in).cuda()
+        c_in64 = c_in.astype(np.float64)
+    if beta == 0.0:
+        out.fill_(float("nan"))  # must not be read
+    announce("gemm_ex", M, N, K, layout, out_dtype, "beta", beta)
+    mx.gemm(*da, *db, alpha=0.25, out=out, layout=layout, m=M, n=N, workspace="auto" if ws else None, beta=beta)
+    if out_dtype == "bf16":
+        got = _bf16_to_f64(host(out.view(torch.int16)).view(np.uint16))
+    else:
+        got = host(out).astype(np.float64)
+    if K:
+        ref, basis = oracle.gemm(aq[:, :K // 2], as_[:, :K // 32], bq[:, :K // 2], bs[:, :K // 32], alpha=0.25,
+                                 with_abs=True)
+    else:
+        ref, basis = np.zeros((M, N)), np.zeros((M, N))
+    if beta != 0.0:
+        ref = ref + beta * c_in64
+        basis = basis + abs(beta) * np.abs(c_in64)
+    if out_dtype == "bf16" and beta == 0.0:
+        # the bf16 result is the FP32 result of the same kernel path rounded to nearest even
+        f32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        mx.gemm(*da, *db, alpha=0.25, out=f32, layout=layout, m=M, n=N, workspace="auto" if ws else None)
+        fb = host(f32).view(np.uint32).astype(np.uint64)
+        rne = ((fb + 0x7FFF + ((fb >> 16) & 1)) >> 16).astype(np.uint16)
+        gb = host(out.view(torch.int16)).view(np.uint16)
+        assert np.array_equal(gb, rne), "bf16 output is not the nearest-even rounding of the FP32 result"
+    bound = TOL * basis + (2.0 ** -8 * (np.abs(ref) + TOL * basis) if out_dtype == "bf16" else 0.0) + 1e-30
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all()
+    assert (err <= bound).all(), "worst err %.3e vs bound %.3e" % (err.max(), bound[np.argmax(err - bound)])
