@@ -57,6 +57,7 @@ def _ptr(a):
 RNE = 0
 SR = 1
 RHT = 0x100  # added to hadamard (16 or 32): randomized Hadamard, signs keyed by the seed
+NOCLIP = 0x10  # added to rounding: the smallest scale that maps the block maximum to <= 6
 
 
 def num_threads() -> int:

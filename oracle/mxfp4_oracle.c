@@ -35,6 +35,8 @@
  *    r < f * 2^32, r being a 32-bit Philox word. Key = (seed mod 2^32, seed >> 32); for the
  *    element at position j of quantized row o (index i = o * L + j, L the quantized length),
  *    counter = (floor(i/4) mod 2^32, floor(i/4) >> 32, stream, 0), word i mod 4.
+ *  - Scale variant "no clip" (rounding argument | 0x10): the smallest scale that maps the block
+ *    maximum to at most 6, i.e. S + 1 exactly when amax > 6 * 2^(S - 127); no element saturates.
  *  - Randomized Hadamard (the pages name it as the other rotation tried, without a construction):
  *    y = H_h (d .* x) per aligned group, with d_j = -1 or +1 for position j along the quantized
  *    axis -- the same for every quantized row, so two operands rotated with the same key keep
@@ -120,6 +122,16 @@ static unsigned e8m0_from_amax(double amax, int nonfinite)
     if (shared < -127) shared = -127;
     if (shared > 127) shared = 127;
     return (unsigned)(shared + 127);
+}
+
+/* The no-clip variant of the scale: the smallest scale byte, from S upward, that maps the block
+ * maximum to at most 6 (the largest E2M1 magnitude), so that no element of the block
+ * saturates. ldexp of 6 by a power of two is exact. */
+static unsigned e8m0_noclip(double amax, unsigned S)
+{
+    if (S == 0xFFu || amax == 0.0) return S;
+    while (S < 254u && amax > ldexp(6.0, (int)S - 127)) ++S;
+    return S;
 }
 
 /* ---------------------------------------------------------------- Philox4x32-10 ------------- */
@@ -212,7 +224,8 @@ static float load_element(const void *x, int dtype, int64_t r, int64_t c, int64_
  * axis = 0: along each column (L = rows), outputs the quantized transpose q[cols][rows/2],
  *           scales[cols][rows/32].
  * h in {0, 16, 32}, or 16 / 32 plus 0x100 for the randomized Hadamard (signs keyed by seed);
- * rounding 0 = nearest-even, 1 = stochastic (Philox). Returns 0 on success.
+ * rounding 0 = nearest-even, 1 = stochastic (Philox), plus 0x10 for the no-clip scale.
+ * Returns 0 on success.
  */
 int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int axis,
                     int h, int rounding, uint64_t seed, uint32_t stream, uint8_t *q, uint8_t *scales)
@@ -220,7 +233,9 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
     const int64_t L = axis ? cols : rows;
     const int64_t outer = axis ? rows : cols;
     const int randomized = (h & 0x100) != 0;
+    const int noclip = (rounding & 0x10) != 0;
     h &= ~0x100;
+    rounding &= ~0x10;
     if (L % 32 != 0 || (h != 0 && h != 16 && h != 32) || (axis != 0 && axis != 1)) return 1;
     if (randomized && h == 0) return 1;
     int status = 0;
@@ -243,6 +258,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
                 else if (fabs((double)blk[t]) > amax) amax = fabs((double)blk[t]);
             }
             unsigned S = e8m0_from_amax(amax, nonfinite);
+            if (noclip) S = e8m0_noclip(amax, S);
             scales[o * (L / 32) + b] = (uint8_t)S;
             for (int t = 0; t < 32; ++t) {
                 unsigned code = 0;

@@ -537,3 +537,51 @@ def test_rht_signs_balanced_and_keyed():
     assert np.array_equal(a, oracle.rht_signs(1, n))
     # prefixes agree: the sign of position j does not depend on how many are requested
     assert np.array_equal(oracle.rht_signs(1, 200), a[:200])
+
+
+# ----------------------------------------------------------------------- no-clip scale ------
+
+def _noclip_scale_by_search(amax):
+    """Smallest S in [0, 254] with amax <= 6 * 2^(S - 127), by exhaustive search (exact)."""
+    if amax == 0.0:
+        return 0
+    for S in range(0, 255):
+        if Fraction(amax) <= 6 * Fraction(2) ** (S - 127):
+            return S
+    return 254
+
+
+def test_noclip_scale_is_the_smallest_without_saturation():
+    """rounding | NOCLIP: every block's scale byte is the smallest with amax <= 6 * scale (found
+    by search over all 255 values), and it differs from the default rule by 0 or 1."""
+    rng = np.random.default_rng(91)
+    blocks = []
+    for m in (1.0, 1.25, 1.5, 1.5000001, 1.75, 1.9999999):     # block max mantissas around 1.5
+        for e in (-130, -126, -125, -124, -3, 0, 5, 100, 126):
+            b = (rng.standard_normal(32) * 0.4 * m * 2.0 ** e).astype(np.float32)
+            b[rng.integers(0, 32)] = np.float32(m * 2.0 ** e) * (1 if rng.random() < 0.5 else -1)
+            blocks.append(b)
+    x = np.concatenate(blocks).reshape(len(blocks), 32).astype(np.float32)
+    _, s_def = oracle.quantize(x, 1, 0, oracle.RNE)
+    q_nc, s_nc = oracle.quantize(x, 1, 0, oracle.RNE | oracle.NOCLIP)
+    for i in range(x.shape[0]):
+        amax = float(np.max(np.abs(x[i].astype(np.float64))))
+        assert s_nc[i, 0] == _noclip_scale_by_search(amax), (i, amax)
+        assert int(s_nc[i, 0]) - int(s_def[i, 0]) in (0, 1)
+    # nothing saturates: every decoded value is within half a grid step of the input
+    deq = oracle.dequantize(q_nc, s_nc)
+    sc = np.exp2(s_nc.astype(np.float64) - 127)
+    assert np.all(np.abs(deq - x) <= np.repeat(sc, 32, axis=1) * 1.0 + 1e-300)
+
+
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_noclip_equals_default_when_nothing_would_clip(rounding):
+    """Blocks whose maximum maps to at most 6 under the default rule get identical bytes."""
+    rng = np.random.default_rng(92)
+    top = (1.5 * np.exp2(rng.integers(-4, 4, (64, 4)))).astype(np.float32)   # block max mantissa 1.5
+    bound = np.repeat(top, 32, axis=1)
+    x = np.clip(rng.standard_normal((64, 128)).astype(np.float32), -0.99 * bound, 0.99 * bound)
+    x[:, ::32] = top                                                     # maps to exactly 6
+    a = oracle.quantize(x, 1, 0, rounding, 3)
+    b = oracle.quantize(x, 1, 0, rounding | oracle.NOCLIP, 3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
