@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 5
+#define MXFP4_ABI_VERSION 6
 
 typedef enum {
     MXFP4_OK = 0,
@@ -66,6 +66,15 @@ typedef enum {
 typedef enum { MXFP4_IN_BF16 = 0, MXFP4_IN_F32 = 1 } mxfp4_dtype_t;
 
 typedef enum { MXFP4_RNE = 0, MXFP4_SR_PHILOX = 1 } mxfp4_rounding_t;
+
+/*
+ * Scale variant: OR into a rounding value (quantize, quantize_dual, linear cfg rnd_a / rnd_b) to
+ * use the smallest scale that maps the block maximum to at most 6 -- S + 1 exactly when
+ * amax > 6 * 2^(S - 127) -- so no element of the block saturates, instead of the OCP rule
+ * S = floor(log2 amax) - 2 whose block maximum can map into [6, 8) and clip to 6. The pages fix
+ * neither; the default follows the OCP MX specification.
+ */
+#define MXFP4_SCALE_NOCLIP 0x10
 
 typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
 

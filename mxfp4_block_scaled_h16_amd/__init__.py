@@ -27,6 +27,7 @@ FPROP, DGRAD, WGRAD = 0, 1, 2
 ROWS, TILED = 0, 1
 BF16, F32 = 0, 1
 RHT = 0x100  # OR into hadamard (16 or 32): randomized Hadamard, signs keyed by the seed
+SCALE_NOCLIP = 0x10  # OR into rounding: the smallest scale that maps the block maximum to <= 6
 
 _lib = None
 
@@ -113,11 +114,20 @@ def _stream(stream):
 
 
 def _rounding(r):
-    if r in (RNE, "rne", "nearest"):
-        return RNE
-    if r in (SR, "sr", "stochastic"):
-        return SR
-    raise ValueError("rounding must be 'rne' or 'sr'")
+    """'rne' / 'sr' (or RNE / SR), optionally '+noclip' (or | SCALE_NOCLIP) for the no-clip scale."""
+    if isinstance(r, str):
+        base, _, extra = r.partition("+")
+        if extra not in ("", "noclip"):
+            raise ValueError("rounding must be 'rne' or 'sr', optionally '+noclip'")
+        flag = SCALE_NOCLIP if extra else 0
+        if base in ("rne", "nearest"):
+            return RNE | flag
+        if base in ("sr", "stochastic"):
+            return SR | flag
+        raise ValueError("rounding must be 'rne' or 'sr', optionally '+noclip'")
+    if int(r) & ~SCALE_NOCLIP in (RNE, SR):
+        return int(r)
+    raise ValueError("rounding must be RNE or SR, optionally | SCALE_NOCLIP")
 
 
 def _layout(layout):

@@ -38,6 +38,15 @@ mxfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP
 // Validation of one quantize call; also used by the linear entry points.
 static_assert(MXFP4_RHT == mx::kRandomizedHadamard, "randomized-Hadamard flag");
 
+// rounding: MXFP4_RNE or MXFP4_SR_PHILOX, optionally with MXFP4_SCALE_NOCLIP
+bool valid_rounding(int rounding)
+{
+    const int r = rounding & ~MXFP4_SCALE_NOCLIP;
+    return r == MXFP4_RNE || r == MXFP4_SR_PHILOX;
+}
+bool is_sr(int rounding) { return (rounding & ~MXFP4_SCALE_NOCLIP) == MXFP4_SR_PHILOX; }
+bool is_noclip(int rounding) { return (rounding & MXFP4_SCALE_NOCLIP) != 0; }
+
 // hadamard: 0, 16 or 32, or 16 / 32 with MXFP4_RHT
 bool valid_rotation(int hadamard)
 {
@@ -56,7 +65,7 @@ mxfp4_status_t check_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
     if (dtype != MXFP4_IN_BF16 && dtype != MXFP4_IN_F32) return MXFP4_ERR_ARG;
     if (axis != 0 && axis != 1) return MXFP4_ERR_ARG;
     if (!valid_rotation(hadamard)) return MXFP4_ERR_ARG;
-    if (rounding != MXFP4_RNE && rounding != MXFP4_SR_PHILOX) return MXFP4_ERR_ARG;
+    if (!valid_rounding(rounding)) return MXFP4_ERR_ARG;
     if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return MXFP4_ERR_SHAPE;
     const int64_t L = axis ? cols : rows;
     const int64_t outer = axis ? rows : cols;
@@ -145,9 +154,7 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     if (!cfg) return MXFP4_ERR_NULL;
     if (M < 0 || K < 0 || N < 0 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return MXFP4_ERR_SHAPE;
     if (!valid_rotation(cfg->hadamard)) return MXFP4_ERR_ARG;
-    if ((cfg->rnd_a != MXFP4_RNE && cfg->rnd_a != MXFP4_SR_PHILOX) ||
-        (cfg->rnd_b != MXFP4_RNE && cfg->rnd_b != MXFP4_SR_PHILOX))
-        return MXFP4_ERR_ARG;
+    if (!valid_rounding(cfg->rnd_a) || !valid_rounding(cfg->rnd_b)) return MXFP4_ERR_ARG;
     if (sp.kc % 32 != 0) return MXFP4_ERR_SHAPE;
     OperandSpace a, b;
     pass_operands(pass, M, K, N, &a, &b);
@@ -184,12 +191,10 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     auto quant = [&](const void *src, int64_t rows, int64_t cols, int axis, mxfp4_rounding_t rnd,
                      uint32_t sid, uint8_t *q, uint8_t *sc, int64_t L) {
         if (axis == 1)
-            return mx::launch_quantize_rows(src, false, rows, cols, cols, cfg->hadamard,
-                                            rnd == MXFP4_SR_PHILOX, cfg->seed, sid, tiled, q, L / 2,
-                                            sc, L / 32, s);
-        return mx::launch_quantize_cols(src, false, rows, cols, cols, cfg->hadamard,
-                                        rnd == MXFP4_SR_PHILOX, cfg->seed, sid, tiled, q, L / 2, sc,
-                                        L / 32, s);
+            return mx::launch_quantize_rows(src, false, rows, cols, cols, cfg->hadamard, is_sr(rnd),
+                                            is_noclip(rnd), cfg->seed, sid, tiled, q, L / 2, sc, L / 32, s);
+        return mx::launch_quantize_cols(src, false, rows, cols, cols, cfg->hadamard, is_sr(rnd),
+                                        is_noclip(rnd), cfg->seed, sid, tiled, q, L / 2, sc, L / 32, s);
     };
     hipError_t e = quant(sp.a_src, sp.a_rows, sp.a_cols, sp.a_axis, cfg->rnd_a, 0u, aq, as, a.L);
     if (e == hipSuccess) e = quant(sp.b_src, sp.b_rows, sp.b_cols, sp.b_axis, cfg->rnd_b, 1u, bq, bs, b.L);
@@ -214,12 +219,12 @@ mxfp4_status_t mxfp4_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, 
     if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
     if ((st = check_device()) != MXFP4_OK) return st;
     const bool f32 = dtype == MXFP4_IN_F32;
-    const bool sr = rounding == MXFP4_SR_PHILOX;
+    const bool sr = is_sr(rounding), noclip = is_noclip(rounding);
     const bool tiled = layout == MXFP4_LAYOUT_TILED;
     hipError_t e = axis == 1
-        ? mx::launch_quantize_rows(x, f32, rows, cols, ldx, hadamard, sr, seed, stream_id, tiled, q,
+        ? mx::launch_quantize_rows(x, f32, rows, cols, ldx, hadamard, sr, noclip, seed, stream_id, tiled, q,
                                    ldq, scales, lds, (hipStream_t)stream)
-        : mx::launch_quantize_cols(x, f32, rows, cols, ldx, hadamard, sr, seed, stream_id, tiled, q,
+        : mx::launch_quantize_cols(x, f32, rows, cols, ldx, hadamard, sr, noclip, seed, stream_id, tiled, q,
                                    ldq, scales, lds, (hipStream_t)stream);
     return from_hip(e);
 }
@@ -238,8 +243,8 @@ mxfp4_status_t mxfp4_quantize_dual(const void *x, mxfp4_dtype_t dtype, int64_t r
     if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
     if ((st = check_device()) != MXFP4_OK) return st;
     const auto conv = [](const mxfp4_quant_out_t &o) {
-        return mx::QuantOut{o.rounding == MXFP4_SR_PHILOX, o.seed, o.stream_id, o.layout == MXFP4_LAYOUT_TILED,
-                            o.q, o.ldq, o.scales, o.lds};
+        return mx::QuantOut{is_sr(o.rounding), is_noclip(o.rounding), o.seed, o.stream_id,
+                            o.layout == MXFP4_LAYOUT_TILED, o.q, o.ldq, o.scales, o.lds};
     };
     return from_hip(mx::launch_quantize_dual(x, dtype == MXFP4_IN_F32, rows, cols, ldx, hadamard, conv(a),
                                              conv(b), (hipStream_t)stream));

@@ -14,18 +14,19 @@ constexpr int kRandomizedHadamard = 0x100;
 // Arguments are validated by the caller; these only pick a kernel and enqueue it.
 // tiled: write the tiled layout (L % 512 == 0; ldq and lds unused), else row-major.
 hipError_t launch_quantize_rows(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
-                                int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
+                                int hadamard, bool stochastic, bool noclip, uint64_t seed, uint32_t stream_id,
                                 bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream);
 
 hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
-                                int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
+                                int hadamard, bool stochastic, bool noclip, uint64_t seed, uint32_t stream_id,
                                 bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream);
 
 // One output of launch_quantize_dual: the same arguments launch_quantize_rows/cols take.
 struct QuantOut {
     bool stochastic;
+    bool noclip;
     uint64_t seed;
     uint32_t stream_id;
     bool tiled;

@@ -66,6 +66,14 @@ __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits)
     return e > 2u ? e - 2u : 0u;
 }
 
+// The no-clip variant: one more when the block maximum maps above 6 under S = max(E - 2, 0),
+// i.e. E >= 2 and the amax significand above 1.5 (then S + 1 maps it into (3, 4)).
+__device__ __forceinline__ uint32_t e8m0_noclip(uint32_t amax_bits, uint32_t s)
+{
+    const bool up = s != 0xFFu && (amax_bits >> 23) >= 2u && (amax_bits & 0x7FFFFFu) > 0x400000u;
+    return s + (up ? 1u : 0u);
+}
+
 // ---------------------------------------------------------------------------- E2M1 encode -----
 // Nearest-even encoding uses gfx950's v_cvt_scalef32_pk_fp4_f32, which converts two binary32
 // values divided by a binary32 scale to two E2M1 codes (first value in the low nibble) with
@@ -98,10 +106,10 @@ __device__ __forceinline__ void prescale_if_zero_scale(float *v, uint32_t s)
     }
 }
 
-// 2^(127 - S) as binary32 multiplier for S in [0, 252] (exponent field 254 - S in [2, 254]).
+// 2^(127 - S) as binary32 multiplier for S in [0, 253] (exponent field 254 - S in [1, 254]).
 __device__ __forceinline__ float e8m0_reciprocal(uint32_t s)
 {
-    const uint32_t sc = s < 252u ? s : 252u;
+    const uint32_t sc = s < 253u ? s : 253u;
     return __uint_as_float((254u - sc) << 23);
 }
 

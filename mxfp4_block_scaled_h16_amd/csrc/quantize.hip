@@ -58,7 +58,7 @@ template <int H, bool F32, bool SR, bool TILED, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t groups_per_row, uint32_t total_groups,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
-    uint32_t key1, uint32_t stream_id, int64_t L)
+    uint32_t key1, uint32_t stream_id, int64_t L, uint32_t noclip)
 {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t base = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * (64u * kRowsUnroll);
@@ -110,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
         for (int i = 0; i < 8; ++i) amax = max(amax, abs_bits(v[u][i]));
         amax = max(amax, quad_xor<1>(amax));
         amax = max(amax, quad_xor<2>(amax));
-        const uint32_t sc = e8m0_from_amax_bits(amax);
+        uint32_t sc = e8m0_from_amax_bits(amax);
+        if (noclip) sc = e8m0_noclip(amax, sc);
         uint32_t word;
         if constexpr (SR) {
             const uint64_t index0 = (uint64_t)row[u] * (uint64_t)L + (uint64_t)grp[u] * 8u;
@@ -152,7 +153,7 @@ template <int H, bool F32, bool SR, bool TILED, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t rows, uint32_t cols, uint32_t col_tiles,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
-    uint32_t key1, uint32_t stream_id)
+    uint32_t key1, uint32_t stream_id, uint32_t noclip)
 {
     constexpr int kEsize = F32 ? 4 : 2;
     constexpr int kTileCols = kColsRowBytes / kEsize;   // 32 f32 or 64 bf16 columns
@@ -221,7 +222,8 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
                 uint32_t amax = 0u;
 #pragma unroll
                 for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[cc][i]));
-                const uint32_t sc = e8m0_from_amax_bits(amax);
+                uint32_t sc = e8m0_from_amax_bits(amax);
+                if (noclip) sc = e8m0_noclip(amax, sc);
                 uint32_t words[4];
                 if constexpr (SR) {
                     const uint64_t index0 = (uint64_t)(c0 + tc) * (uint64_t)rows + (uint64_t)(r0 + 32 * blk);
@@ -286,7 +288,7 @@ struct DualOut {
     uint8_t *scales;
     int64_t lds;
     uint32_t key0, key1, stream_id;
-    uint32_t sr, tiled;
+    uint32_t sr, tiled, noclip;
 };
 
 template <int H, bool F32, bool RHT>
@@ -363,7 +365,8 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
             for (int i = 0; i < 8; ++i) amax = max(amax, abs_bits(v[i]));
             amax = max(amax, quad_xor<1>(amax));
             amax = max(amax, quad_xor<2>(amax));
-            const uint32_t sc = e8m0_from_amax_bits(amax);
+            uint32_t sc = e8m0_from_amax_bits(amax);
+            if (o1.noclip) sc = e8m0_noclip(amax, sc);
             const uint32_t o = r0 + tr, g = g1;   // quantized row, global group
             uint32_t word;
             if (o1.sr) {
@@ -413,7 +416,8 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
             uint32_t amax = 0u;
 #pragma unroll
             for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[cc][i]));
-            const uint32_t sc = e8m0_from_amax_bits(amax);
+            uint32_t sc = e8m0_from_amax_bits(amax);
+            if (o0.noclip) sc = e8m0_noclip(amax, sc);
             uint32_t words[4];
             if (o0.sr) {
                 const uint64_t index0 = (uint64_t)(c0 + tc) * rows + r0 + 32 * blk;
@@ -482,27 +486,27 @@ hipError_t dual_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx,
 template <int H, bool F32, bool SR, bool TILED, bool RHT>
 hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
-                         hipStream_t stream)
+                         bool noclip, hipStream_t stream)
 {
     const uint32_t gpr = (uint32_t)(cols / 8);
     const uint32_t total = (uint32_t)(rows * (cols / 8));
     const uint32_t per_block = kThreads * kRowsUnroll;
     const dim3 grid((total + per_block - 1) / per_block);
     return launch(quant_rows_kernel<H, F32, SR, TILED, RHT>, grid, dim3(kThreads), 0, stream, x, ldx, gpr, total, q,
-                  ldq, scales, lds, (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, cols);
+                  ldq, scales, lds, (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, cols, noclip ? 1u : 0u);
 }
 
 template <int H, bool F32, bool SR, bool TILED, bool RHT>
 hipError_t cols_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
-                         hipStream_t stream)
+                         bool noclip, hipStream_t stream)
 {
     const int64_t tile_cols = kColsRowBytes / (F32 ? 4 : 2);
     const int64_t col_tiles = (cols + tile_cols - 1) / tile_cols;
     const int64_t row_tiles = (rows + kColsTileRows - 1) / kColsTileRows;
     return launch(quant_cols_kernel<H, F32, SR, TILED, RHT>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0,
                   stream, x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles, q, ldq, scales, lds,
-                  (uint32_t)seed, (uint32_t)(seed >> 32), stream_id);
+                  (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, noclip ? 1u : 0u);
 }
 
 template <template <int, bool, bool> class Sel, typename... A>
@@ -549,21 +553,21 @@ struct ColsSel {
 }  // namespace
 
 hipError_t launch_quantize_rows(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
-                                int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
+                                int hadamard, bool stochastic, bool noclip, uint64_t seed, uint32_t stream_id,
                                 bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream)
 {
     return pick<RowsSel>(hadamard & kHadamardSize, f32, stochastic, tiled, (hadamard & kRandomizedHadamard) != 0,
-                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, stream);
+                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, noclip, stream);
 }
 
 hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
-                                int hadamard, bool stochastic, uint64_t seed, uint32_t stream_id,
+                                int hadamard, bool stochastic, bool noclip, uint64_t seed, uint32_t stream_id,
                                 bool tiled, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                                 hipStream_t stream)
 {
     return pick<ColsSel>(hadamard & kHadamardSize, f32, stochastic, tiled, (hadamard & kRandomizedHadamard) != 0,
-                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, stream);
+                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, noclip, stream);
 }
 
 hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
@@ -572,7 +576,7 @@ hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t c
 {
     const auto conv = [](const QuantOut &o) {
         return DualOut{o.q, o.ldq, o.scales, o.lds, (uint32_t)o.seed, (uint32_t)(o.seed >> 32), o.stream_id,
-                       o.stochastic ? 1u : 0u, o.tiled ? 1u : 0u};
+                       o.stochastic ? 1u : 0u, o.tiled ? 1u : 0u, o.noclip ? 1u : 0u};
     };
     const DualOut o1 = conv(axis1), o0 = conv(axis0);
     const bool rht = (hadamard & kRandomizedHadamard) != 0;

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 5
+    assert L.mxfp4_abi_version() == 6
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -97,6 +97,8 @@ def test_quantize_argument_errors(L):
     assert _q(L, h=0x300) == 3                              # unknown flag bit
     assert _q(L, axis=2) == 3
     assert _q(L, rnd=5) == 3
+    assert _q(L, rnd=0x11, x=None) == 1                    # SR | MXFP4_SCALE_NOCLIP is valid
+    assert _q(L, rnd=0x12) == 3
     assert _q(L, dtype=3) == 3
     assert _q(L, ldx=32) == 3                               # ldx < cols
     assert _q(L, ldq=16) == 3                               # ldq < L/2

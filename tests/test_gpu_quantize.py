@@ -172,3 +172,21 @@ def test_randomized_hadamard_bit_exact(axis, h, rounding):
         rq, rs = oracle.quantize(x, axis=axis, hadamard=h | oracle.RHT, rounding=rounding, seed=seed, stream=1)
         assert np.array_equal(sh, rs), "rht scales differ"
         assert np.array_equal(qh, rq), "rht codes differ"
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_noclip_scale_bit_exact(axis, rounding):
+    """rounding | MXFP4_SCALE_NOCLIP, with blocks whose maximum would clip under the default rule
+    (significand above 1.5), at tiny, ordinary and huge magnitudes."""
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(95 + axis + rounding)
+    x = rng.standard_normal((128, 256)).astype(np.float32)
+    x[:, ::7] *= np.float32(1.7)
+    x[0:4, :] *= np.float32(2.0 ** 120)
+    x[4:8, :] *= np.float32(2.0 ** -120)
+    x[8, :] = np.float32(1.75 * 2.0 ** 127)                    # scale byte 253 under no-clip
+    xin = x if axis == 1 else np.ascontiguousarray(x.T)
+    for h in (0, 16):
+        check(xin, axis, h, rounding | mx.SCALE_NOCLIP, seed=4, what="noclip")
+    check(inputs.bf16_bits(xin), axis, 32, rounding | mx.SCALE_NOCLIP, seed=4, what="noclip bf16")

@@ -145,3 +145,12 @@ def test_dual_randomized_hadamard(h):
         x = inputs.bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32) * 2)
         check_dual(x, h | mx.RHT, r1, r0, seed1=41, seed0=42, stream1=0, stream0=1, lay1=lay1, lay0=lay0,
                    what="rht")
+
+
+def test_dual_noclip_scale():
+    """The no-clip scale on either output, with the other on the default rule."""
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(801)
+    x = inputs.bf16_bits((rng.standard_normal((256, 512)) * 1.7).astype(np.float32))
+    check_dual(x, 16, 0 | mx.SCALE_NOCLIP, 1, seed0=5, what="noclip rows")
+    check_dual(x, 16, 1, 0 | mx.SCALE_NOCLIP, seed1=6, lay1="tiled", what="noclip cols")
