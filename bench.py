@@ -457,8 +457,8 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the sharding plan is written up in DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path. Use --gpus 1.",
+              file=sys.stderr)
         return 2
     import numpy as np
     import torch
