@@ -63,6 +63,8 @@ def parse_args():
                    help="skip the vendor GEMM baselines (hipBLASLt MXFP8 / MXFP4 / FP8 / bf16)")
     p.add_argument("--separate-quant", action="store_true",
                    help="one quantizer launch per axis instead of one dual launch per tensor")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured HBM and matrix-core ceilings")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -408,6 +410,54 @@ def run_timed(plan, steps, warmup):
     return (t1 - t0) * 1e3 / steps, per_launch.mean(0)
 
 
+def machine_ceilings(settle_s=0.25, reps=10):
+    """Practical ceilings of this board, measured in the same run with the plain kernels of
+    libmxfp4_ceiling.so: streaming HBM read, write and copy of 1 GiB buffers (16-byte accesses,
+    GB/s of bytes moved), and the scaled FP4 MFMA loop on register-resident operands that change
+    every round, one 8-wavefront workgroup per compute unit (TFLOP/s). Each is settled for
+    `settle_s` seconds, then `reps` launches are timed with fence-free events."""
+    import torch
+    from mxfp4_block_scaled_h16_amd import ceiling
+    ev = TimingEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ceiling.write(src, 0x5A5AA5A5)  # every lane's XOR of equal 16-byte words is 0, never 1
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    msink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    iters = 3000
+    cases = [
+        ("hbm_read_gbs", lambda: ceiling.read(src, 1, sink), nbytes),
+        ("hbm_write_gbs", lambda: ceiling.write(dst, 0x01234567), nbytes),
+        ("hbm_copy_gbs", lambda: ceiling.copy(src, dst), 2 * nbytes),
+        ("mfma_fp4_tflops", lambda: ceiling.mfma(cus, iters, 7, msink), cus * iters * ceiling.MFMA_FLOPS_PER_ROUND),
+    ]
+    out = {}
+    for name, f, work in cases:
+        t_end = time.perf_counter() + settle_s
+        while time.perf_counter() < t_end:
+            f()
+            torch.cuda.synchronize()
+        a, b = ev.create(), ev.create()
+        ev.record(a, stream)
+        for _ in range(reps):
+            f()
+        ev.record(b, stream)
+        torch.cuda.synchronize()
+        t = ev.elapsed_ms(a, b) * 1e-3 / reps
+        out[name] = round(work / t / (1e12 if name.startswith("mfma") else 1e9), 1)
+    ev.close()
+    if not bool(torch.isfinite(msink).all()):
+        raise RuntimeError("matrix-core ceiling kernel produced non-finite sums")
+    out["note"] = ("measured in this run: 1 GiB streaming read / write / copy (copy counts read + write bytes); "
+                   "scaled FP4 32x32x64 MFMA loop, %d workgroups x 8 wavefronts, operands changing every round"
+                   % cus)
+    del src, dst, msink
+    return out
+
+
 def library_baselines(M, N, K, steps, settle_s=0.25):
     """Vendor GEMMs (hipBLASLt through torch._scaled_mm / torch.mm) at one product shape, as
     context: block-scaled MXFP8 and MXFP4 (E8M0 scale per 32 along K), per-tensor FP8 and
@@ -540,6 +590,13 @@ def main():
         buf2.copy_(buf)
         torch.cuda.synchronize()
 
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = machine_ceilings()
+        roofline["ceiling"] = ceilings["mfma_fp4_tflops"]
+        roofline["frac_of_ceiling"] = round(achieved / ceilings["mfma_fp4_tflops"], 4)
+        quantizer["frac_of_copy_ceiling"] = round(q_bytes / q_s / 1e9 / ceilings["hbm_copy_gbs"], 4)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(plan, h)
 
     sizes = ", ".join("%s K=%d N=%d" % (n, k, nn) for n, k, nn in projs)
@@ -559,6 +616,8 @@ def main():
     }
     if fprop is not None:
         line["fprop_only"] = fprop
+    if ceilings is not None:
+        line["ceilings"] = ceilings
     if baselines is not None:
         line["library_baselines"] = baselines
     print(json.dumps(line), flush=True)

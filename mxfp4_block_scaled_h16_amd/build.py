@@ -1,4 +1,5 @@
-"""Build the HIP library libmxfp4.so in-tree for gfx950 with hipcc."""
+"""Build the HIP libraries in-tree for gfx950 with hipcc: libmxfp4.so (the quantizers, GEMMs and
+C ABI) and libmxfp4_ceiling.so (the HBM and matrix-core ceiling kernels the benchmark reports)."""
 import os
 import shutil
 import subprocess
@@ -9,6 +10,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp4.so")
 SOURCES = ["api.cpp", "quantize.hip", "gemm.hip"]
 HEADERS = ["internal.h", "mx_device.h"]
+CEILING_LIB = os.path.join(HERE, "libmxfp4_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -40,15 +43,23 @@ def is_stale() -> bool:
     return any(os.path.getmtime(f) > t for f in _inputs())
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    if not force and not is_stale():
-        return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _compile(sources, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    if force or is_stale():
+        _compile(SOURCES, LIB, verbose)
+    ceiling_inputs = [os.path.join(CSRC, s) for s in CEILING_SOURCES]
+    ceiling_inputs.append(os.path.join(HERE, "..", "include", "mxfp4_ceiling.h"))
+    if force or not os.path.exists(CEILING_LIB) or any(
+            os.path.getmtime(f) > os.path.getmtime(CEILING_LIB) for f in ceiling_inputs):
+        _compile(CEILING_SOURCES, CEILING_LIB, verbose)
     return LIB
 
 

@@ -9,10 +9,11 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+CEILING_HEADER = os.path.join(ROOT, "include", "mxfp4_ceiling.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mxfp4_[a-z0-9_]+)\s*\(", text)))
 
@@ -36,6 +37,28 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
+
+
+def test_ceiling_library_exports_its_declared_symbols():
+    """libmxfp4_ceiling.so (the benchmark's HBM and matrix-core ceiling kernels) loads and exports
+    what include/mxfp4_ceiling.h declares; invalid sizes and NULL pointers are rejected before any
+    launch."""
+    from mxfp4_block_scaled_h16_amd import ceiling
+    C = ceiling.lib()
+    names = declared_functions(CEILING_HEADER)
+    assert names == ["mxfp4_ceiling_copy", "mxfp4_ceiling_mfma", "mxfp4_ceiling_read", "mxfp4_ceiling_write"]
+    for name in names:
+        assert hasattr(C, name), name
+    fake = 1 << 20  # never dereferenced: every call below fails its host-side checks
+    assert C.mxfp4_ceiling_read(None, 16, 0, fake, None) == 1
+    assert C.mxfp4_ceiling_read(fake, 15, 0, fake, None) == 2
+    assert C.mxfp4_ceiling_read(fake + 4, 16, 0, fake, None) == 2
+    assert C.mxfp4_ceiling_write(fake, 0, 0, None) == 2
+    assert C.mxfp4_ceiling_copy(fake, None, 16, None) == 1
+    assert C.mxfp4_ceiling_copy(fake, fake + 8, 16, None) == 2
+    assert C.mxfp4_ceiling_mfma(0, 1, 0, fake, None) == 2
+    assert C.mxfp4_ceiling_mfma(1, 0, 0, fake, None) == 2
+    assert C.mxfp4_ceiling_mfma(1, 1, 0, None, None) == 1
 
 
 def test_abi_version_and_status_strings(L):
