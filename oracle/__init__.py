@@ -57,6 +57,7 @@ def _ptr(a):
 RNE = 0
 SR = 1
 RHT = 0x100  # added to hadamard (16 or 32): randomized Hadamard, signs keyed by the seed
+ORTHO = 0x200  # added to hadamard (16 or 32): orthonormal rotation H_h / sqrt(h)
 NOCLIP = 0x10  # added to rounding: the smallest scale that maps the block maximum to <= 6
 
 
@@ -89,7 +90,8 @@ def rht_signs(seed, count):
 
 def quantize(x, axis=1, hadamard=16, rounding=RNE, seed=0, stream=0):
     """MXFP4-quantize a 2-D array along ``axis`` after the block Hadamard rotation
-    (``hadamard`` 16 or 32 plus ``RHT``: the randomized Hadamard with signs keyed by ``seed``).
+    (``hadamard`` 16 or 32, plus ``RHT``: the randomized Hadamard with signs keyed by ``seed``,
+    and / or plus ``ORTHO``: the orthonormal H_h / sqrt(h)).
 
     x: uint16 (bf16 bit patterns) or float32, shape (rows, cols).
     Returns (codes uint8 [outer, L/2], scales uint8 [outer, L/32]) with L the quantized length
@@ -157,7 +159,9 @@ def gemm_sampled(aq, as_, bq, bs, ms, ns, alpha=1.0):
 
 def alpha_for(hadamard):
     """H_h H_h^T = h I (and (H D)(H D)^T = h I for a +-1 diagonal D), so a product of two
-    rotated operands carries a factor h."""
+    rotated operands carries a factor h; the orthonormal rotation H_h / sqrt(h) carries none."""
+    if int(hadamard) & ORTHO:
+        return 1.0
     h = int(hadamard) & ~RHT
     return 1.0 / h if h else 1.0
 

@@ -44,6 +44,11 @@
  *    Philox4x32-10 with key (seed mod 2^32, seed >> 32) and counter (floor(j/128) mod 2^32,
  *    floor(j/128) >> 32, 0, 1) is set (the last counter word 1 keeps it apart from the
  *    stochastic-rounding words, whose last counter word is 0).
+ *  - Orthonormal rotation (hadamard | 0x200; the pages name the 16x16 and 32x32 matrices without
+ *    a normalisation): y = H_h x / sqrt(h), computed as the binary32 transform above followed by
+ *    one binary32 multiplication of every value by the binary32 number nearest to 1/sqrt(h)
+ *    (0.25 for h = 16, exact; 2^-2.5 rounded for h = 32). A product of two such operands needs no
+ *    1/h factor.
  *  - GEMM: C[m][n] = alpha * sum_k deq(A)[m][k] * deq(B)[n][k]; each 32-element block product is
  *    an exact integer sum, scaled exactly, and blocks are summed in binary64.
  *
@@ -223,7 +228,8 @@ static float load_element(const void *x, int dtype, int64_t r, int64_t c, int64_
  * axis = 1: along each row (L = cols), outputs q[rows][cols/2], scales[rows][cols/32].
  * axis = 0: along each column (L = rows), outputs the quantized transpose q[cols][rows/2],
  *           scales[cols][rows/32].
- * h in {0, 16, 32}, or 16 / 32 plus 0x100 for the randomized Hadamard (signs keyed by seed);
+ * h in {0, 16, 32}, or 16 / 32 plus 0x100 for the randomized Hadamard (signs keyed by seed)
+ * and / or plus 0x200 for the orthonormal scaling H_h / sqrt(h);
  * rounding 0 = nearest-even, 1 = stochastic (Philox), plus 0x10 for the no-clip scale.
  * Returns 0 on success.
  */
@@ -233,11 +239,15 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
     const int64_t L = axis ? cols : rows;
     const int64_t outer = axis ? rows : cols;
     const int randomized = (h & 0x100) != 0;
+    const int orthonormal = (h & 0x200) != 0;
     const int noclip = (rounding & 0x10) != 0;
-    h &= ~0x100;
+    h &= ~0x300;
     rounding &= ~0x10;
     if (L % 32 != 0 || (h != 0 && h != 16 && h != 32) || (axis != 0 && axis != 1)) return 1;
-    if (randomized && h == 0) return 1;
+    if ((randomized || orthonormal) && h == 0) return 1;
+    /* binary32 nearest to 1/sqrt(h): sqrt and division are correctly rounded in binary64, and
+     * 1/sqrt(h) is nowhere near a binary32 rounding boundary for h = 16, 32 */
+    const float norm = orthonormal ? (float)(1.0 / sqrt((double)h)) : 1.0f;
     int status = 0;
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t o = 0; o < outer; ++o) {
@@ -249,6 +259,8 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
             for (int64_t j = 0; j < L; ++j)
                 if (rht_negate(seed, (uint64_t)j)) y[j] = -y[j];  /* exact */
         if (h) oracle_fwht_binary32(y, L, h);
+        if (orthonormal)
+            for (int64_t j = 0; j < L; ++j) y[j] = y[j] * norm; /* one binary32 multiply */
         for (int64_t b = 0; b < L / 32; ++b) {
             const float *blk = y + 32 * b;
             double amax = 0.0;

@@ -585,3 +585,64 @@ def test_noclip_equals_default_when_nothing_would_clip(rounding):
     a = oracle.quantize(x, 1, 0, rounding, 3)
     b = oracle.quantize(x, 1, 0, rounding | oracle.NOCLIP, 3)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ orthonormal rotation -----
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_ortho_h16_is_the_unnormalised_rotation_two_binades_down(axis, rounding):
+    """H16 / 4 scales every rotated value by an exact power of two: the codes are those of the
+    unnormalised H16 and every scale byte is 2 lower (normal-range inputs, so nothing underflows;
+    the SR words are the same because they depend only on the position)."""
+    rng = np.random.default_rng(93)
+    x = inputs.bf16_bits((rng.standard_normal((64, 96)) * 3).astype(np.float32))
+    a = oracle.quantize(x, axis, 16, rounding, 5, 1)
+    b = oracle.quantize(x, axis, 16 | oracle.ORTHO, rounding, 5, 1)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].astype(int) - 2, b[1].astype(int))
+
+
+@pytest.mark.parametrize("h", [16, 32])
+def test_ortho_unit_vectors_closed_form(h):
+    """x = e_k inside each h-group: H_h e_k / sqrt(h) is column k of H_h times 1/sqrt(h), so a
+    block's amax is 1/sqrt(h), the scale byte 127 + floor(log2(1/sqrt(h))) - 2 (122 for h = 32,
+    123 for h = 16), every magnitude 2^(127 - S) / sqrt(h) (5.66 -> 6 for h = 32, exactly 4 for
+    h = 16) and the signs those of (-1)^popcount(j & k). Scaling by 1/h or not at all gives other
+    bytes."""
+    L = 64
+    x = np.zeros((h, L), dtype=np.float32)
+    for k in range(h):
+        x[k, k::h] = 1.0      # e_k in every h-group of row k
+    q, s = oracle.quantize(x, 1, h | oracle.ORTHO, 0)
+    S = 127 + math.floor(math.log2(1.0 / math.sqrt(h))) - 2
+    assert (s == S).all()
+    mag = 2.0 ** (127 - S) / math.sqrt(h)
+    want_mag = {16: 6, 32: 7}[h]            # 4.0 is index 6; 5.66 rounds to 6.0, index 7
+    assert abs(mag - {16: 4.0, 32: 5.656854249492381}[h]) < 1e-12
+    codes = unpack_codes(q)
+    for k in range(h):
+        for j in range(L):
+            neg = bin((j % h) & k).count("1") % 2 == 1
+            assert codes[k, j] == (8 if neg else 0) | want_mag
+
+
+@pytest.mark.parametrize("h", [16, 32])
+def test_ortho_keeps_the_norm_and_the_product(h):
+    """An orthonormal rotation keeps each row's energy: the dequantized rows carry the input's
+    sum of squares up to the MXFP4 error; and the forward GEMM of two orthonormally rotated
+    operands needs no 1/h factor (alpha 1) to approximate X W^T."""
+    rng = np.random.default_rng(94)
+    x = rng.standard_normal((32, 256)).astype(np.float32)
+    w = (rng.standard_normal((48, 256)) * 0.02).astype(np.float32)
+    q, s = oracle.quantize(x, 1, h | oracle.ORTHO, 0)
+    ratio = (oracle.dequantize(q, s) ** 2).sum(axis=1) / (x.astype(np.float64) ** 2).sum(axis=1)
+    assert np.all(np.abs(ratio - 1.0) < 0.15), ratio
+    assert oracle.alpha_for(h | oracle.ORTHO) == 1.0 and oracle.alpha_for(h | oracle.ORTHO | oracle.RHT) == 1.0
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    err = lambda y: np.linalg.norm(y - ref) / np.linalg.norm(ref)  # noqa: E731
+    e_ortho = err(oracle.linear_fprop(x, w, h | oracle.ORTHO))
+    e_plain = err(oracle.linear_fprop(x, w, h))
+    # MXFP4 on both operands of a K = 256 product of Gaussians: ~17% relative error either way;
+    # a product off by a factor h (a missing or doubled 1/h) would be off by 94% or more
+    assert e_ortho < 0.3 and abs(e_ortho - e_plain) < 0.1, (e_ortho, e_plain)
