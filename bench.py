@@ -79,8 +79,10 @@ class Plan:
         desc, projs, passes, M = WORKLOADS[workload]
         self.mx, self.torch, self.h, self.passes, self.M = mx, torch, h, passes, M
         self.dual = dual
-        # h may carry the randomized-Hadamard flag; alpha undoes the factor of the size alone
-        self.alpha = 1.0 / (h & ~mx.RHT) if h & ~mx.RHT else 1.0
+        # h may carry the randomized-Hadamard or orthonormal flags; alpha undoes the factor of the
+        # size alone (the orthonormal rotation leaves none)
+        hs = h & ~(mx.RHT | mx.ORTHO)
+        self.alpha = 1.0 if (h & mx.ORTHO) or not hs else 1.0 / hs
         dev = "cuda"
         to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
         # host tensors (bf16 bit patterns), drawn by the shared seeded recipe

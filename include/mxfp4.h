@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 6
+#define MXFP4_ABI_VERSION 7
 
 typedef enum {
     MXFP4_OK = 0,
@@ -91,6 +91,18 @@ typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
 #define MXFP4_RHT 0x100
 
 /*
+ * Orthonormal rotation: OR this flag into a hadamard size of 16 or 32 (with or without
+ * MXFP4_RHT) to rotate by H_h / sqrt(h) instead of H_h. The binary32 transform is followed by one
+ * binary32 multiplication of every rotated value by the binary32 number nearest to 1/sqrt(h)
+ * (1/4 for h = 16, exact: the codes are those of H16 and every scale byte is 2 lower; 2^-2.5
+ * rounded for h = 32, which changes the rounding). A product of two such operands needs no 1/h
+ * factor, so the linear entry points use alpha = 1. The pages (gist.science summary of "MXFP4
+ * LLM pretraining", section 방법론) name 16x16 and 32x32 Hadamard matrices without a
+ * normalisation; the unnormalised H with alpha = 1/h is this library's default reading.
+ */
+#define MXFP4_ORTHONORMAL 0x200
+
+/*
  * Memory layout of a quantized operand with `outer` quantized rows of length L.
  *
  * MXFP4_LAYOUT_ROWS: row-major. codes q[outer][ldq] bytes (the first L/2 used: element j of row o
@@ -124,7 +136,8 @@ mxfp4_status_t mxfp4_tiled_sizes(int64_t outer, int64_t L, size_t *codes_bytes, 
  *   axis=0   quantize along each column (L = rows) and write the quantized TRANSPOSE:
  *                                                  q[cols][ldq], scales[cols][lds]
  *            (the Wgrad token axis and the Dgrad weight operand).
- *   hadamard 0 (no rotation), 16 or 32, or 16 / 32 | MXFP4_RHT (randomized, signs keyed by seed);
+ *   hadamard 0 (no rotation), 16 or 32, or 16 / 32 | MXFP4_RHT (randomized, signs keyed by seed)
+ *            and / or | MXFP4_ORTHONORMAL (H_h / sqrt(h));
  *            rounding MXFP4_RNE or MXFP4_SR_PHILOX with (seed, stream).
  *   layout   MXFP4_LAYOUT_ROWS (q, ldq, scales, lds as above) or MXFP4_LAYOUT_TILED (see above).
  *
@@ -219,7 +232,8 @@ size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Per-operand configuration of one linear-layer GEMM. */
 typedef struct {
-    int hadamard;              /* 0, 16 or 32 (| MXFP4_RHT): rotation along the contraction axis */
+    int hadamard;              /* 0, 16 or 32 (| MXFP4_RHT, | MXFP4_ORTHONORMAL): rotation along
+                                  the contraction axis */
     mxfp4_rounding_t rnd_a;    /* rounding of the first operand (X, dY, dY^T) */
     mxfp4_rounding_t rnd_b;    /* rounding of the second operand (W, W^T, X^T) */
     uint64_t seed;             /* Philox key for stochastic rounding; stream 0 = first operand,

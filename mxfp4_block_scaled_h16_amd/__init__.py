@@ -14,8 +14,8 @@ import os
 import torch  # imported first: the library binds to the HIP runtime torch has loaded
 
 __all__ = [
-    "Mxfp4Error", "RHT", "quantize", "quantize_dual", "gemm", "linear_fprop", "linear_dgrad", "linear_wgrad",
-    "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD", "ROWS", "TILED",
+    "Mxfp4Error", "RHT", "ORTHO", "SCALE_NOCLIP", "quantize", "quantize_dual", "gemm", "linear_fprop",
+    "linear_dgrad", "linear_wgrad", "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD", "ROWS", "TILED",
     "tiled_sizes", "gemm_workspace_bytes",
 ]
 
@@ -27,6 +27,7 @@ FPROP, DGRAD, WGRAD = 0, 1, 2
 ROWS, TILED = 0, 1
 BF16, F32 = 0, 1
 RHT = 0x100  # OR into hadamard (16 or 32): randomized Hadamard, signs keyed by the seed
+ORTHO = 0x200  # OR into hadamard (16 or 32): orthonormal rotation H_h / sqrt(h) (GEMM alpha 1)
 SCALE_NOCLIP = 0x10  # OR into rounding: the smallest scale that maps the block maximum to <= 6
 
 _lib = None

@@ -37,6 +37,7 @@ mxfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP
 
 // Validation of one quantize call; also used by the linear entry points.
 static_assert(MXFP4_RHT == mx::kRandomizedHadamard, "randomized-Hadamard flag");
+static_assert(MXFP4_ORTHONORMAL == mx::kOrthonormal, "orthonormal-rotation flag");
 
 // rounding: MXFP4_RNE or MXFP4_SR_PHILOX, optionally with MXFP4_SCALE_NOCLIP
 bool valid_rounding(int rounding)
@@ -47,12 +48,13 @@ bool valid_rounding(int rounding)
 bool is_sr(int rounding) { return (rounding & ~MXFP4_SCALE_NOCLIP) == MXFP4_SR_PHILOX; }
 bool is_noclip(int rounding) { return (rounding & MXFP4_SCALE_NOCLIP) != 0; }
 
-// hadamard: 0, 16 or 32, or 16 / 32 with MXFP4_RHT
+// hadamard: 0, 16 or 32, or 16 / 32 with MXFP4_RHT and / or MXFP4_ORTHONORMAL
 bool valid_rotation(int hadamard)
 {
-    const int h = hadamard & ~MXFP4_RHT;
+    const int flags = MXFP4_RHT | MXFP4_ORTHONORMAL;
+    const int h = hadamard & ~flags;
     if (h != 0 && h != 16 && h != 32) return false;
-    return !((hadamard & MXFP4_RHT) && h == 0);
+    return !((hadamard & flags) && h == 0);
 }
 
 mxfp4_status_t check_quantize(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
@@ -165,9 +167,10 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     if (sp.out_rows == 0 || sp.out_cols == 0) return MXFP4_OK;
     if (!out) return MXFP4_ERR_NULL;
     if (!aligned(out, 4)) return MXFP4_ERR_ALIGN;
-    // H H^T = h I, also with the randomized sign diagonal (D D^T = I)
-    const int h = cfg->hadamard & ~MXFP4_RHT;
-    const float alpha = h ? 1.0f / (float)h : 1.0f;
+    // H H^T = h I, also with the randomized sign diagonal (D D^T = I); the orthonormal rotation
+    // (H / sqrt(h)) (H / sqrt(h))^T = I needs no factor
+    const int h = cfg->hadamard & ~(MXFP4_RHT | MXFP4_ORTHONORMAL);
+    const float alpha = (cfg->hadamard & MXFP4_ORTHONORMAL) || h == 0 ? 1.0f : 1.0f / (float)h;
     if (sp.kc == 0) {
         // empty contraction: the product is all zeros
         if (mxfp4_status_t st = check_device()) return st;

@@ -7,9 +7,10 @@
 namespace mx {
 
 // hadamard argument of the launchers: the size (0, 16, 32) in the low byte, plus the
-// randomized-Hadamard flag (the public MXFP4_RHT).
+// randomized-Hadamard flag (the public MXFP4_RHT) and the orthonormal flag.
 constexpr int kHadamardSize = 0xFF;
 constexpr int kRandomizedHadamard = 0x100;
+constexpr int kOrthonormal = 0x200;  // rotate by H_h / sqrt(h) (the public MXFP4_ORTHONORMAL)
 
 // Arguments are validated by the caller; these only pick a kernel and enqueue it.
 // tiled: write the tiled layout (L % 512 == 0; ldq and lds unused), else row-major.

@@ -53,6 +53,14 @@ __device__ __forceinline__ void rotate_block(float *v)
     }
 }
 
+// v[i] *= s in binary32 (the orthonormal rotation's 1/sqrt(h), after the transform)
+template <int N>
+__device__ __forceinline__ void scale_values(float *v, float s)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = v[i] * s;
+}
+
 // ---------------------------------------------------------------------------- scale -----------
 // |x| as an unsigned bit pattern orders like |x|, with NaN above +inf.
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }

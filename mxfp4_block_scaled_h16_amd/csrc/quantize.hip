@@ -58,7 +58,7 @@ template <int H, bool F32, bool SR, bool TILED, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t groups_per_row, uint32_t total_groups,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
-    uint32_t key1, uint32_t stream_id, int64_t L, uint32_t noclip)
+    uint32_t key1, uint32_t stream_id, int64_t L, uint32_t noclip, float norm)
 {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t base = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * (64u * kRowsUnroll);
@@ -104,6 +104,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
             fwht_regs<8>(v[u]);
             fwht_cross_stage<1>(v[u], upper1);
             if constexpr (H == 32) fwht_cross_stage<2>(v[u], upper2);
+            if (norm != 1.0f) scale_values<8>(v[u], norm);
         }
         uint32_t amax = 0u;
 #pragma unroll
@@ -153,7 +154,7 @@ template <int H, bool F32, bool SR, bool TILED, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t rows, uint32_t cols, uint32_t col_tiles,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
-    uint32_t key1, uint32_t stream_id, uint32_t noclip)
+    uint32_t key1, uint32_t stream_id, uint32_t noclip, float norm)
 {
     constexpr int kEsize = F32 ? 4 : 2;
     constexpr int kTileCols = kColsRowBytes / kEsize;   // 32 f32 or 64 bf16 columns
@@ -219,6 +220,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
                 const uint32_t tc = cp * kColsPerThread + cc;  // tile column = quantized row
                 if constexpr (RHT) apply_signs<32>(v[cc], signs);
                 rotate_block<H>(v[cc]);
+                if (H > 0 && norm != 1.0f) scale_values<32>(v[cc], norm);
                 uint32_t amax = 0u;
 #pragma unroll
                 for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[cc][i]));
@@ -294,7 +296,7 @@ struct DualOut {
 template <int H, bool F32, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t rows, uint32_t cols, uint32_t col_tiles,
-    DualOut o1, DualOut o0)
+    DualOut o1, DualOut o0, float norm)
 {
     constexpr int kEsize = F32 ? 4 : 2;
     constexpr int kRowBytes = kDualTile * kEsize;
@@ -359,6 +361,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
                 fwht_regs<8>(v);
                 fwht_cross_stage<1>(v, upper1);
                 if constexpr (H == 32) fwht_cross_stage<2>(v, upper2);
+                if (norm != 1.0f) scale_values<8>(v, norm);
             }
             uint32_t amax = 0u;
 #pragma unroll
@@ -413,6 +416,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
             const uint32_t tc = F32 ? lane + 64 * cc : 2 * lane + cc;  // tile column = quantized row
             if constexpr (RHT) apply_signs<32>(v[cc], col_signs);
             rotate_block<H>(v[cc]);
+            if (H > 0 && norm != 1.0f) scale_values<32>(v[cc], norm);
             uint32_t amax = 0u;
 #pragma unroll
             for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[cc][i]));
@@ -475,38 +479,47 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
 
 template <int H, bool F32, bool RHT>
 hipError_t dual_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, const DualOut &o1,
-                         const DualOut &o0, hipStream_t stream)
+                         const DualOut &o0, float norm, hipStream_t stream)
 {
     const int64_t col_tiles = (cols + kDualTile - 1) / kDualTile;
     const int64_t row_tiles = (rows + kDualTile - 1) / kDualTile;
     return launch(quant_dual_kernel<H, F32, RHT>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0, stream,
-                  x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles, o1, o0);
+                  x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles, o1, o0, norm);
 }
 
 template <int H, bool F32, bool SR, bool TILED, bool RHT>
 hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
-                         bool noclip, hipStream_t stream)
+                         bool noclip, float norm, hipStream_t stream)
 {
     const uint32_t gpr = (uint32_t)(cols / 8);
     const uint32_t total = (uint32_t)(rows * (cols / 8));
     const uint32_t per_block = kThreads * kRowsUnroll;
     const dim3 grid((total + per_block - 1) / per_block);
     return launch(quant_rows_kernel<H, F32, SR, TILED, RHT>, grid, dim3(kThreads), 0, stream, x, ldx, gpr, total, q,
-                  ldq, scales, lds, (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, cols, noclip ? 1u : 0u);
+                  ldq, scales, lds, (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, cols, noclip ? 1u : 0u, norm);
 }
 
 template <int H, bool F32, bool SR, bool TILED, bool RHT>
 hipError_t cols_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint64_t seed,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
-                         bool noclip, hipStream_t stream)
+                         bool noclip, float norm, hipStream_t stream)
 {
     const int64_t tile_cols = kColsRowBytes / (F32 ? 4 : 2);
     const int64_t col_tiles = (cols + tile_cols - 1) / tile_cols;
     const int64_t row_tiles = (rows + kColsTileRows - 1) / kColsTileRows;
     return launch(quant_cols_kernel<H, F32, SR, TILED, RHT>, dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0,
                   stream, x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles, q, ldq, scales, lds,
-                  (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, noclip ? 1u : 0u);
+                  (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, noclip ? 1u : 0u, norm);
+}
+
+// orthonormal rotation (hadamard | kOrthonormal): the binary32 number nearest to 1/sqrt(h) that
+// multiplies every rotated value (h = 16: 1/4 exactly; h = 32: 2^-2.5 = sqrt(2) / 8 rounded to
+// binary32); 1 for the unnormalised H, which the kernels skip
+float rotation_norm(int hadamard)
+{
+    if (!(hadamard & kOrthonormal)) return 1.0f;
+    return (hadamard & kHadamardSize) == 16 ? 0.25f : 0x1.6a09e6p-3f;
 }
 
 template <template <int, bool, bool> class Sel, typename... A>
@@ -558,7 +571,8 @@ hipError_t launch_quantize_rows(const void *x, bool f32, int64_t rows, int64_t c
                                 hipStream_t stream)
 {
     return pick<RowsSel>(hadamard & kHadamardSize, f32, stochastic, tiled, (hadamard & kRandomizedHadamard) != 0,
-                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, noclip, stream);
+                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, noclip, rotation_norm(hadamard),
+                         stream);
 }
 
 hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
@@ -567,7 +581,8 @@ hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t c
                                 hipStream_t stream)
 {
     return pick<ColsSel>(hadamard & kHadamardSize, f32, stochastic, tiled, (hadamard & kRandomizedHadamard) != 0,
-                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, noclip, stream);
+                         x, rows, cols, ldx, seed, stream_id, q, ldq, scales, lds, noclip, rotation_norm(hadamard),
+                         stream);
 }
 
 hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
@@ -579,18 +594,19 @@ hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t c
                        o.stochastic ? 1u : 0u, o.tiled ? 1u : 0u, o.noclip ? 1u : 0u};
     };
     const DualOut o1 = conv(axis1), o0 = conv(axis0);
+    const float norm = rotation_norm(hadamard);
     const bool rht = (hadamard & kRandomizedHadamard) != 0;
     switch ((hadamard & kHadamardSize) * 4 + (f32 ? 2 : 0) + (rht ? 1 : 0)) {
-    case 0: return dual_dispatch<0, false, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 2: return dual_dispatch<0, true, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 64: return dual_dispatch<16, false, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 65: return dual_dispatch<16, false, true>(x, rows, cols, ldx, o1, o0, stream);
-    case 66: return dual_dispatch<16, true, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 67: return dual_dispatch<16, true, true>(x, rows, cols, ldx, o1, o0, stream);
-    case 128: return dual_dispatch<32, false, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 129: return dual_dispatch<32, false, true>(x, rows, cols, ldx, o1, o0, stream);
-    case 130: return dual_dispatch<32, true, false>(x, rows, cols, ldx, o1, o0, stream);
-    case 131: return dual_dispatch<32, true, true>(x, rows, cols, ldx, o1, o0, stream);
+    case 0: return dual_dispatch<0, false, false>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 2: return dual_dispatch<0, true, false>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 64: return dual_dispatch<16, false, false>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 65: return dual_dispatch<16, false, true>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 66: return dual_dispatch<16, true, false>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 67: return dual_dispatch<16, true, true>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 128: return dual_dispatch<32, false, false>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 129: return dual_dispatch<32, false, true>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 130: return dual_dispatch<32, true, false>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 131: return dual_dispatch<32, true, true>(x, rows, cols, ldx, o1, o0, norm, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -62,7 +62,7 @@ def test_ceiling_library_exports_its_declared_symbols():
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 6
+    assert L.mxfp4_abi_version() == 7
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -100,6 +100,8 @@ def test_quantize_dual_argument_errors(L):
     assert _dual(L, rows=48) == 2                          # axis-0 length (rows) % 32
     assert _dual(L, cols=48, ldx=48) == 2                  # axis-1 length (cols) % 32
     assert _dual(L, h=8) == 3
+    assert _dual(L, h=0x200) == 3
+    assert _dual(L, h=0x220, null1=True) == 1              # valid rotation, then the NULL output
     assert _dual(L, out1=dict(rounding=4)) == 3
     assert _dual(L, out0=dict(layout=7)) == 3
     assert _dual(L, out0=dict(ldq=16)) == 3                # ldq < rows/2 for the transpose
@@ -117,7 +119,11 @@ def test_quantize_argument_errors(L):
     assert _q(L, h=8) == 3                                  # hadamard size
     assert _q(L, h=0x100) == 3                              # randomized flag needs a size
     assert _q(L, h=0x110, x=None) == 1                      # 16 | MXFP4_RHT is a valid rotation
-    assert _q(L, h=0x300) == 3                              # unknown flag bit
+    assert _q(L, h=0x300) == 3                              # flags without a size
+    assert _q(L, h=0x200) == 3                              # orthonormal flag needs a size
+    assert _q(L, h=0x220, x=None) == 1                      # 32 | MXFP4_ORTHONORMAL is valid
+    assert _q(L, h=0x310, x=None) == 1                      # 16 | MXFP4_RHT | MXFP4_ORTHONORMAL
+    assert _q(L, h=0x400 | 16) == 3                         # unknown flag bit
     assert _q(L, axis=2) == 3
     assert _q(L, rnd=5) == 3
     assert _q(L, rnd=0x11, x=None) == 1                    # SR | MXFP4_SCALE_NOCLIP is valid
@@ -162,6 +168,10 @@ def test_linear_argument_errors(L):
     ws = mx.workspace_bytes(mx.FPROP, 64, 64, 64)
     assert f(1 << 12, 1 << 12, 64, 64, 64, None, 1 << 12, ws, 1 << 12, None) == 1
     assert f(1 << 12, 1 << 12, 64, 64, 64, ctypes.byref(bad), 1 << 12, ws, 1 << 12, None) == 3
+    ortho_only = mx.LinearCfg(0x200, 0, 0, 0)                # orthonormal flag without a size
+    assert f(1 << 12, 1 << 12, 64, 64, 64, ctypes.byref(ortho_only), 1 << 12, ws, 1 << 12, None) == 3
+    ortho32 = mx.LinearCfg(0x220, 0, 0, 0)
+    assert f(None, 1 << 12, 64, 64, 64, ctypes.byref(ortho32), 1 << 12, ws, 1 << 12, None) == 1
     assert f(1 << 12, 1 << 12, 64, 48, 64, ctypes.byref(cfg), 1 << 12, ws, 1 << 12, None) == 2
     assert f(1 << 12, 1 << 12, 64, 64, 64, ctypes.byref(cfg), 1 << 12, ws - 1, 1 << 12, None) == 5
     assert f(1 << 12, 1 << 12, 64, 64, 64, ctypes.byref(cfg), None, ws, 1 << 12, None) == 5

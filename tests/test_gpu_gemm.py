@@ -229,6 +229,32 @@ def test_linear_randomized_hadamard(kind, h):
     assert_gemm_close(got, ref, basis, TOL, "rht %s h%d" % (kind, h))
 
 
+@pytest.mark.parametrize("kind", ["fprop", "dgrad", "wgrad"])
+@pytest.mark.parametrize("h", [16, 32])
+def test_linear_orthonormal_rotation(kind, h):
+    """The three linear GEMMs with hadamard = h | MXFP4_ORTHONORMAL (alpha 1; Wgrad also with
+    the randomized signs and SR), every output against the oracle."""
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(90 + h)
+    M, K, N = 256, 512, 384
+    x = inputs.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = inputs.bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    dy = inputs.bf16_bits((rng.standard_t(3, (M, N)) * 1e-3).astype(np.float32))
+    seed = 0xBEEF + h
+    announce("linear ortho", kind, h)
+    if kind == "fprop":
+        got = host(mx.linear_fprop(bf16_dev(x), bf16_dev(w), h | mx.ORTHO, seed=seed))
+        ref, basis = oracle.linear_fprop(x, w, hadamard=h | oracle.ORTHO, seed=seed, with_abs=True)
+    elif kind == "dgrad":
+        got = host(mx.linear_dgrad(bf16_dev(dy), bf16_dev(w), h | mx.ORTHO, seed=seed))
+        ref, basis = oracle.linear_dgrad(dy, w, hadamard=h | oracle.ORTHO, seed=seed, with_abs=True)
+    else:
+        got = host(mx.linear_wgrad(bf16_dev(dy), bf16_dev(x), h | mx.ORTHO | mx.RHT, "sr", "sr", seed))
+        ref, basis = oracle.linear_wgrad(dy, x, hadamard=h | oracle.ORTHO | oracle.RHT, rnd_a=oracle.SR,
+                                         rnd_b=oracle.SR, seed=seed, with_abs=True)
+    assert_gemm_close(got, ref, basis, TOL, "ortho %s h%d" % (kind, h))
+
+
 def _bf16_to_f64(t_u16):
     return (np.asarray(t_u16, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
 

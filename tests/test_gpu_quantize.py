@@ -190,3 +190,30 @@ def test_noclip_scale_bit_exact(axis, rounding):
     for h in (0, 16):
         check(xin, axis, h, rounding | mx.SCALE_NOCLIP, seed=4, what="noclip")
     check(inputs.bf16_bits(xin), axis, 32, rounding | mx.SCALE_NOCLIP, seed=4, what="noclip bf16")
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_orthonormal_rotation_bit_exact(axis, rounding):
+    """hadamard = h | MXFP4_ORTHONORMAL (H_h / sqrt(h)), alone and with the randomized signs,
+    bf16 and f32 inputs with tiny, ordinary and huge magnitudes (the 1/sqrt(h) multiply must
+    round, underflow and saturate as the oracle's binary32 multiply does), both layouts."""
+    from tests.gpu_util import untile
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(120 + axis + rounding)
+    x = rng.standard_normal((128, 512)).astype(np.float32) * 3
+    x[0:4, :] *= np.float32(2.0 ** 120)
+    x[4:8, :] *= np.float32(2.0 ** -130)                        # rotated values near the subnormals
+    xin = x if axis == 1 else np.ascontiguousarray(x.T)
+    for h in (16, 32):
+        check(xin, axis, h | mx.ORTHO, rounding, seed=6, what="ortho f32")
+        check(inputs.bf16_bits(xin), axis, h | mx.ORTHO | mx.RHT, rounding, seed=7, what="ortho rht bf16")
+    # tiled layout
+    shape = (256, 1024) if axis == 1 else (1024, 256)
+    xb = inputs.bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    announce("quantize ortho tiled", shape, "axis", axis, "rnd", rounding)
+    q, s = mx.quantize(bf16_dev(xb), axis=axis, hadamard=32 | mx.ORTHO, rounding=rounding, seed=9, stream_id=1,
+                       layout="tiled")
+    qh, sh = untile(host(q), host(s), 256, 1024)
+    rq, rs = oracle.quantize(xb, axis=axis, hadamard=32 | oracle.ORTHO, rounding=rounding, seed=9, stream=1)
+    assert np.array_equal(sh, rs) and np.array_equal(qh, rq)

@@ -154,3 +154,16 @@ def test_dual_noclip_scale():
     x = inputs.bf16_bits((rng.standard_normal((256, 512)) * 1.7).astype(np.float32))
     check_dual(x, 16, 0 | mx.SCALE_NOCLIP, 1, seed0=5, what="noclip rows")
     check_dual(x, 16, 1, 0 | mx.SCALE_NOCLIP, seed1=6, lay1="tiled", what="noclip cols")
+
+
+def test_dual_orthonormal_rotation():
+    """hadamard = h | MXFP4_ORTHONORMAL on both outputs of the one-pass quantizer (with and
+    without the randomized signs), nearest and SR, rows and tiled layouts."""
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(802)
+    for h in (16, 32):
+        x = inputs.bf16_bits((rng.standard_normal((256, 512)) * 2).astype(np.float32))
+        check_dual(x, h | mx.ORTHO, 0, 1, seed0=11, what="ortho")
+        check_dual(x, h | mx.ORTHO | mx.RHT, 1, 0, seed1=12, seed0=13, lay1="tiled", lay0="rows", what="ortho rht")
+    xf = (rng.standard_normal((160, 96)) * 5).astype(np.float32)
+    check_dual(xf, 32 | mx.ORTHO, 1, 1, seed1=14, seed0=15, what="ortho f32 ragged")
