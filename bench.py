@@ -269,6 +269,44 @@ def measured_traffic(workload):
         return None
 
 
+def quantization_error(plan, rows=8):
+    """Error of the method itself (MXFP4 with the step's rotation and rounding against the exact
+    product): for each GEMM of the last step, ||C - C_exact|| / ||C_exact|| (Frobenius) over
+    `rows` evenly spaced output rows, C_exact the binary64 product of the unquantized bf16
+    inputs (numpy on the host, outside any timed region)."""
+    import numpy as np
+    f64 = {}
+
+    def host64(key, a):
+        if key not in f64:
+            f64[key] = (np.asarray(a, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+        return f64[key]
+    acts, per_proj = plan.host["acts"], plan.host["proj"]
+    out = {}
+    for label, kind, spec, _ in plan.op_list:
+        if kind != "gemm":
+            continue
+        qa, qb, okey = spec
+        name, pas = okey
+        w = host64(("w", name), per_proj[name][0])
+        dy = host64(("dy", name), per_proj[name][1])
+        akey = qb[0] if pas == "W" else qa[0]
+        x = host64(("x", akey), acts[akey]) if pas in "FW" else None
+        got = plan.out[okey]
+        idx = np.linspace(0, got.shape[0] - 1, rows).round().astype(np.int64)
+        c = got[plan.torch.from_numpy(idx).to(got.device)].cpu().numpy().astype(np.float64)
+        if pas == "F":
+            ref = x[idx] @ w.T
+        elif pas == "D":
+            ref = dy[idx] @ w
+        else:
+            ref = dy[:, idx].T @ x
+        out[label] = round(float(np.linalg.norm(c - ref) / np.linalg.norm(ref)), 5)
+    out["rows_sampled"] = rows
+    out["reference"] = "binary64 product of the unquantized bf16 inputs"
+    return out
+
+
 def cpu_baseline(plan, h):
     """The oracle, untuned, on a bounded sample of the same step, projected to the whole step."""
     import numpy as np
@@ -599,6 +637,7 @@ def main():
         roofline["frac_of_ceiling"] = round(achieved / ceilings["mfma_fp4_tflops"], 4)
         quantizer["frac_of_copy_ceiling"] = round(q_bytes / q_s / 1e9 / ceilings["hbm_copy_gbs"], 4)
 
+    qerr = quantization_error(plan, rows=8 if len(plan.op_list) < 12 else 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline(plan, h)
 
     sizes = ", ".join("%s K=%d N=%d" % (n, k, nn) for n, k, nn in projs)
@@ -618,6 +657,7 @@ def main():
     }
     if fprop is not None:
         line["fprop_only"] = fprop
+    line["quantization_error"] = qerr
     if ceilings is not None:
         line["ceilings"] = ceilings
     if baselines is not None:

@@ -76,3 +76,15 @@ def test_qkv_step_sampled():
     Wgrad, dual quantizers, tiled operands): 2048 sampled outputs per GEMM plus the corners."""
     plan = _run_plan("qkv", 16, True)
     _check_outputs(plan, 16, samples=2048)
+
+
+def test_quantization_error_report():
+    """The benchmark's method-error figure on the small workload: every GEMM is reported, and
+    each relative error is that of MXFP4 (a few to a few tens of percent), neither 0 nor 1."""
+    import bench
+    plan = _run_plan("small", 16, True)
+    err = bench.quantization_error(plan, rows=8)
+    labels = [label for label, kind, _, _ in plan.op_list if kind == "gemm"]
+    assert set(labels) <= set(err)
+    for label in labels:
+        assert 0.005 < err[label] < 0.35, (label, err[label])
