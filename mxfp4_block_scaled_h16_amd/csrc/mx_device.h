@@ -230,16 +230,16 @@ __device__ __forceinline__ uint32_t quad_xor(uint32_t v)
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, true);
 }
 
-// One Walsh-Hadamard stage whose pairs straddle lanes l and l ^ X (each lane holds 8 values,
+// One Walsh-Hadamard stage whose pairs straddle lanes l and l ^ X (each lane holds N values,
 // the lane with bit X set holds the higher-index element of every pair): the lower lane keeps
 // u + w, the upper lane u - w, computed as u + (-w) (IEEE subtraction), so the results are
 // bit-identical to the in-register stage.
-template <int X>
+template <int X, int N = 8>
 __device__ __forceinline__ void fwht_cross_stage(float *v, bool upper)
 {
     const uint32_t flip = upper ? 0x80000000u : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N; ++i) {
         const float other = __uint_as_float(quad_xor<X>(__float_as_uint(v[i])));
         v[i] = other + __uint_as_float(__float_as_uint(v[i]) ^ flip);
     }

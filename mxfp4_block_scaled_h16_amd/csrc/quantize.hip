@@ -17,28 +17,31 @@ namespace {
 constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------------------ quant_rows --
-// A lane owns 8 consecutive elements (16 bytes of bf16, 32 of f32); lanes 4b .. 4b + 3 own one
-// 32-element MX block, so every load instruction of a wavefront reads 64 consecutive 8-element
-// groups. Hadamard stages of stride 1, 2, 4 run in registers, the stride-8 and stride-16
-// stages across lanes l ^ 1 and l ^ 2; the block amax is reduced over the same quad. Each lane
-// stores one 32-bit word of codes (consecutive lanes, consecutive words) and lane 4b the scale.
-constexpr int kRowsUnroll = 4;  // 8-element groups per lane, 64 groups apart
+// A lane owns 16 consecutive elements (32 bytes of bf16, 64 of f32); lanes 2b, 2b + 1 own one
+// 32-element MX block, so a wavefront covers 64 consecutive 16-element groups. H16 runs entirely
+// in registers; H32's stride-16 stage crosses to lane l ^ 1, and so does the block amax. Each
+// lane stores 8 bytes of codes (consecutive lanes, consecutive bytes) and lane 2b the scale.
+constexpr int kRowsUnroll = 2;  // 16-element groups per lane, 64 groups apart
 
 template <bool F32>
-__device__ __forceinline__ void load8(const char *p, float *v)
+__device__ __forceinline__ void load16(const char *p, float *v)
 {
     if constexpr (F32) {
-        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + 1);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            v[2 * u] = bf16_lo(w[u]);
-            v[2 * u + 1] = bf16_hi(w[u]);
+        for (int k = 0; k < 4; ++k) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(p + 16 * k);
+            v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const u32x4 t = *reinterpret_cast<const u32x4 *>(p + 16 * k);
+            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v[8 * k + 2 * u] = bf16_lo(w[u]);
+                v[8 * k + 2 * u + 1] = bf16_hi(w[u]);
+            }
         }
     }
 }
@@ -63,17 +66,17 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t base = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * (64u * kRowsUnroll);
     const size_t esize = F32 ? 4 : 2;
-    const bool upper1 = lane & 1, upper2 = lane & 2;
+    const bool upper1 = lane & 1;
 
-    float v[kRowsUnroll][8];
+    float v[kRowsUnroll][16];
     uint32_t row[kRowsUnroll], grp[kRowsUnroll];
     bool live[kRowsUnroll];
     {
-        // every lane runs (the cross-lane stages need the whole quad); a group past the end is
-        // replaced by one of the last block, same lane within the quad, and is not stored
+        // every lane runs (the cross-lane steps need both lanes of a block); a group past the end
+        // is replaced by one of the last block, same lane within the pair, and is not stored
         uint32_t g = base + lane;
         live[0] = g < total_groups;
-        if (!live[0]) g = total_groups - 4u + (lane & 3u);
+        if (!live[0]) g = total_groups - 2u + (lane & 1u);
         uint32_t r = g / groups_per_row;
         uint32_t c = g - r * groups_per_row;
 #pragma unroll
@@ -88,48 +91,54 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
                         ++r;
                     }
                 } else {
-                    r = (total_groups - 4u) / groups_per_row;
-                    c = total_groups - 4u + (lane & 3u) - r * groups_per_row;
+                    r = (total_groups - 2u) / groups_per_row;
+                    c = total_groups - 2u + (lane & 1u) - r * groups_per_row;
                 }
             }
             row[u] = r;
             grp[u] = c;
-            load8<F32>(reinterpret_cast<const char *>(x) + ((int64_t)r * ldx + (int64_t)c * 8) * esize, v[u]);
         }
+        // all loads in flight before any is consumed
+#pragma unroll
+        for (int u = 0; u < kRowsUnroll; ++u)
+            load16<F32>(reinterpret_cast<const char *>(x) + ((int64_t)row[u] * ldx + (int64_t)grp[u] * 16) * esize,
+                        v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kRowsUnroll; ++u) {
-        if constexpr (RHT) apply_signs<8>(v[u], (rht_sign_word(grp[u] / 4, key0, key1) >> (8 * (grp[u] % 4))) & 0xFFu);
+        if constexpr (RHT) apply_signs<16>(v[u], (rht_sign_word(grp[u] / 2, key0, key1) >> (16 * (grp[u] % 2))) & 0xFFFFu);
         if constexpr (H >= 16) {
-            fwht_regs<8>(v[u]);
-            fwht_cross_stage<1>(v[u], upper1);
-            if constexpr (H == 32) fwht_cross_stage<2>(v[u], upper2);
-            if (norm != 1.0f) scale_values<8>(v[u], norm);
+            fwht_regs<16>(v[u]);
+            if constexpr (H == 32) fwht_cross_stage<1, 16>(v[u], upper1);
+            if (norm != 1.0f) scale_values<16>(v[u], norm);
         }
         uint32_t amax = 0u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = max(amax, abs_bits(v[u][i]));
+        for (int i = 0; i < 16; ++i) amax = max(amax, abs_bits(v[u][i]));
         amax = max(amax, quad_xor<1>(amax));
-        amax = max(amax, quad_xor<2>(amax));
         uint32_t sc = e8m0_from_amax_bits(amax);
         if (noclip) sc = e8m0_noclip(amax, sc);
-        uint32_t word;
+        uint32_t w0, w1;
         if constexpr (SR) {
-            const uint64_t index0 = (uint64_t)row[u] * (uint64_t)L + (uint64_t)grp[u] * 8u;
-            word = encode8_stochastic(v[u], sc, index0, key0, key1, stream_id);
+            const uint64_t index0 = (uint64_t)row[u] * (uint64_t)L + (uint64_t)grp[u] * 16u;
+            w0 = encode8_stochastic(v[u], sc, index0, key0, key1, stream_id);
+            w1 = encode8_stochastic(v[u] + 8, sc, index0 + 8u, key0, key1, stream_id);
         } else {
-            prescale_if_zero_scale<8>(v[u], sc);
-            word = encode8_nearest(v[u], e8m0_divisor(sc));
+            prescale_if_zero_scale<16>(v[u], sc);
+            const float div = e8m0_divisor(sc);
+            w0 = encode8_nearest(v[u], div);
+            w1 = encode8_nearest(v[u] + 8, div);
         }
-        if (sc == 0xFFu) word = 0u;
+        if (sc == 0xFFu) w0 = w1 = 0u;
+        const u32x2 codes = {w0, w1};
         if (live[u]) {
             if constexpr (TILED) {
-                const int64_t at = tiled_chunk(row[u], grp[u] / 4, L) + 4 * (grp[u] % 4);
-                __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(q + at));
-                if ((lane & 3u) == 0u) scales[tiled_scale(row[u], grp[u] / 4, L)] = (uint8_t)sc;
+                const int64_t at = tiled_chunk(row[u], grp[u] / 2, L) + 8 * (grp[u] % 2);
+                __builtin_nontemporal_store(codes, reinterpret_cast<u32x2 *>(q + at));
+                if ((lane & 1u) == 0u) scales[tiled_scale(row[u], grp[u] / 2, L)] = (uint8_t)sc;
             } else {
-                __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(q + (int64_t)row[u] * ldq) + grp[u]);
-                if ((lane & 3u) == 0u) scales[(int64_t)row[u] * lds + grp[u] / 4] = (uint8_t)sc;
+                __builtin_nontemporal_store(codes, reinterpret_cast<u32x2 *>(q + (int64_t)row[u] * ldq) + grp[u]);
+                if ((lane & 1u) == 0u) scales[(int64_t)row[u] * lds + grp[u] / 2] = (uint8_t)sc;
             }
         }
     }
@@ -492,8 +501,8 @@ hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx,
                          uint32_t stream_id, uint8_t *q, int64_t ldq, uint8_t *scales, int64_t lds,
                          bool noclip, float norm, hipStream_t stream)
 {
-    const uint32_t gpr = (uint32_t)(cols / 8);
-    const uint32_t total = (uint32_t)(rows * (cols / 8));
+    const uint32_t gpr = (uint32_t)(cols / 16);
+    const uint32_t total = (uint32_t)(rows * (cols / 16));
     const uint32_t per_block = kThreads * kRowsUnroll;
     const dim3 grid((total + per_block - 1) / per_block);
     return launch(quant_rows_kernel<H, F32, SR, TILED, RHT>, grid, dim3(kThreads), 0, stream, x, ldx, gpr, total, q,
