@@ -280,9 +280,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 // each column (axis 0, written as the quantized transpose). Across Fprop, Dgrad and Wgrad each of
 // X, W and dY is a contraction operand along both of its axes, so a training step needs both.
 // A workgroup takes a 128 x 128-element tile:
-//  1. a lane loads 8 consecutive elements of a row (16 lanes per row, 4 rows per wavefront
+//  1. a lane loads 16 consecutive elements of a row (8 lanes per row, 8 rows per wavefront
 //     load), keeps the raw bits in an LDS tile and quantizes them along the row as quant_rows
-//     does (in-register and quad-crossing Hadamard stages, quad amax, one code word per lane);
+//     does (Hadamard in registers, H32's last stage and the block amax across the lane pair,
+//     8 bytes of codes per lane);
 //  2. after a barrier a lane reads two columns of one 32-row block (one 32-bit LDS word per row;
 //     the 64 lanes of a wavefront read one 256-byte row, all banks distinct), rotates, scales
 //     and encodes them as quant_cols does; after a barrier (every lane holds its columns) the
@@ -309,8 +310,8 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
 {
     constexpr int kEsize = F32 ? 4 : 2;
     constexpr int kRowBytes = kDualTile * kEsize;
-    constexpr int kParts = F32 ? 2 : 1;           // 16-byte pieces per 8-element group
-    constexpr int kSteps = kDualTile / 16;        // row loads per lane
+    constexpr int kParts = F32 ? 4 : 2;           // 16-byte pieces per 16-element group
+    constexpr int kSteps = kDualTile / 32;        // row loads per lane (8 rows per wavefront each)
     __shared__ __attribute__((aligned(16))) uint8_t tile[kDualTile * kRowBytes];
     uint8_t *out = tile;                          // reused once the tile has been read
     uint8_t *out_scales = tile + kDualTile * 64;
@@ -324,78 +325,83 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
 
     // 1. load, keep, quantize along the rows
     {
-        const uint32_t gi = lane % 16;          // 8-element group within the tile row
-        const bool col_live = gi * 8 < ncols;   // a quad (one MX block) lives or dies whole
-        const bool upper1 = lane & 1, upper2 = lane & 2;
+        const uint32_t gi = lane % 8;           // 16-element group within the tile row
+        const bool col_live = gi * 16 < ncols;  // a lane pair (one MX block) lives or dies whole
+        const bool upper1 = lane & 1;
         // a lane outside the tensor loads an element inside it instead (row and group clamped):
         // the loads stay unconditional, and whatever it computes from them is never stored
-        const uint32_t lg = min(gi, ncols / 8u - 1u);
+        const uint32_t lg = min(gi, ncols / 16u - 1u);
         u32x4 raw[kSteps][kParts];
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
-            const uint32_t lr = min(16u * k + 4u * wave + lane / 16u, nrows - 1u);
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(xb + ((int64_t)(r0 + lr) * ldx + c0 + 8 * lg) * kEsize);
+            const uint32_t lr = min(32u * k + 8u * wave + lane / 8u, nrows - 1u);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(xb + ((int64_t)(r0 + lr) * ldx + c0 + 16 * lg) * kEsize);
+            // plain loads: of a lane's 32 (64) bytes, the later 16-byte pieces come from L1
 #pragma unroll
-            for (int p = 0; p < kParts; ++p) raw[k][p] = __builtin_nontemporal_load(src + p);
+            for (int p = 0; p < kParts; ++p) raw[k][p] = src[p];
         }
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
-            const uint32_t tr = 16 * k + 4 * wave + lane / 16;
-            u32x4 *dst = reinterpret_cast<u32x4 *>(tile + tr * kRowBytes + gi * 8 * kEsize);
+            const uint32_t tr = 32 * k + 8 * wave + lane / 8;
+            u32x4 *dst = reinterpret_cast<u32x4 *>(tile + tr * kRowBytes + gi * 16 * kEsize);
 #pragma unroll
             for (int p = 0; p < kParts; ++p) dst[p] = raw[k][p];
         }
-        // randomized rotation: this lane's 8 positions along the rows are the same for every k
-        const uint32_t g1 = c0 / 8 + gi;
-        const uint32_t row_signs = RHT ? (rht_sign_word(g1 / 4, o1.key0, o1.key1) >> (8 * (g1 % 4))) & 0xFFu : 0u;
+        // randomized rotation: this lane's 16 positions along the rows are the same for every k
+        const uint32_t g1 = c0 / 16 + gi;
+        const uint32_t row_signs =
+            RHT ? (rht_sign_word(g1 / 2, o1.key0, o1.key1) >> (16 * (g1 % 2))) & 0xFFFFu : 0u;
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
-            const uint32_t tr = 16 * k + 4 * wave + lane / 16;
-            float v[8];
-            if constexpr (F32) {
-                const uint32_t w[8] = {raw[k][0].x, raw[k][0].y, raw[k][0].z, raw[k][0].w,
-                                       raw[k][1].x, raw[k][1].y, raw[k][1].z, raw[k][1].w};
+            const uint32_t tr = 32 * k + 8 * wave + lane / 8;
+            float v[16];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
-            } else {
-                const uint32_t w[4] = {raw[k][0].x, raw[k][0].y, raw[k][0].z, raw[k][0].w};
+            for (int p = 0; p < kParts; ++p) {
+                const uint32_t w[4] = {raw[k][p].x, raw[k][p].y, raw[k][p].z, raw[k][p].w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    v[2 * u] = bf16_lo(w[u]);
-                    v[2 * u + 1] = bf16_hi(w[u]);
+                    if constexpr (F32) {
+                        v[4 * p + u] = __uint_as_float(w[u]);
+                    } else {
+                        v[8 * p + 2 * u] = bf16_lo(w[u]);
+                        v[8 * p + 2 * u + 1] = bf16_hi(w[u]);
+                    }
                 }
             }
-            if constexpr (RHT) apply_signs<8>(v, row_signs);
+            if constexpr (RHT) apply_signs<16>(v, row_signs);
             if constexpr (H >= 16) {
-                fwht_regs<8>(v);
-                fwht_cross_stage<1>(v, upper1);
-                if constexpr (H == 32) fwht_cross_stage<2>(v, upper2);
-                if (norm != 1.0f) scale_values<8>(v, norm);
+                fwht_regs<16>(v);
+                if constexpr (H == 32) fwht_cross_stage<1, 16>(v, upper1);
+                if (norm != 1.0f) scale_values<16>(v, norm);
             }
             uint32_t amax = 0u;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) amax = max(amax, abs_bits(v[i]));
+            for (int i = 0; i < 16; ++i) amax = max(amax, abs_bits(v[i]));
             amax = max(amax, quad_xor<1>(amax));
-            amax = max(amax, quad_xor<2>(amax));
             uint32_t sc = e8m0_from_amax_bits(amax);
             if (o1.noclip) sc = e8m0_noclip(amax, sc);
-            const uint32_t o = r0 + tr, g = g1;   // quantized row, global group
-            uint32_t word;
+            const uint32_t o = r0 + tr, g = g1;   // quantized row, global 16-element group
+            uint32_t w0, w1;
             if (o1.sr) {
-                word = encode8_stochastic(v, sc, (uint64_t)o * cols + 8u * g, o1.key0, o1.key1, o1.stream_id);
+                const uint64_t index0 = (uint64_t)o * cols + 16u * g;
+                w0 = encode8_stochastic(v, sc, index0, o1.key0, o1.key1, o1.stream_id);
+                w1 = encode8_stochastic(v + 8, sc, index0 + 8u, o1.key0, o1.key1, o1.stream_id);
             } else {
-                prescale_if_zero_scale<8>(v, sc);
-                word = encode8_nearest(v, e8m0_divisor(sc));
+                prescale_if_zero_scale<16>(v, sc);
+                const float div = e8m0_divisor(sc);
+                w0 = encode8_nearest(v, div);
+                w1 = encode8_nearest(v + 8, div);
             }
-            if (sc == 0xFFu) word = 0u;
+            if (sc == 0xFFu) w0 = w1 = 0u;
+            const u32x2 codes = {w0, w1};
             if (col_live && tr < nrows) {
                 if (o1.tiled) {
-                    const int64_t at = tiled_chunk(o, g / 4, cols) + 4 * (g % 4);
-                    __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(o1.q + at));
-                    if ((lane & 3u) == 0u) o1.scales[tiled_scale(o, g / 4, cols)] = (uint8_t)sc;
+                    const int64_t at = tiled_chunk(o, g / 2, cols) + 8 * (g % 2);
+                    __builtin_nontemporal_store(codes, reinterpret_cast<u32x2 *>(o1.q + at));
+                    if ((lane & 1u) == 0u) o1.scales[tiled_scale(o, g / 2, cols)] = (uint8_t)sc;
                 } else {
-                    __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(o1.q + (int64_t)o * o1.ldq) + g);
-                    if ((lane & 3u) == 0u) o1.scales[(int64_t)o * o1.lds + g / 4] = (uint8_t)sc;
+                    __builtin_nontemporal_store(codes, reinterpret_cast<u32x2 *>(o1.q + (int64_t)o * o1.ldq) + g);
+                    if ((lane & 1u) == 0u) o1.scales[(int64_t)o * o1.lds + g / 2] = (uint8_t)sc;
                 }
             }
         }
