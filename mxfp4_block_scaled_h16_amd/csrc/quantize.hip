@@ -21,28 +21,41 @@ constexpr int kThreads = 256;
 // 32-element MX block, so a wavefront covers 64 consecutive 16-element groups. H16 runs entirely
 // in registers; H32's stride-16 stage crosses to lane l ^ 1, and so does the block amax. Each
 // lane stores 8 bytes of codes (consecutive lanes, consecutive bytes) and lane 2b the scale.
+// bf16 loads stay fully coalesced: each of a wavefront's two 16-byte loads reads 64 consecutive
+// 8-element halves (lane l the half l / 32 of groups l % 32 and 32 + l % 32), and one
+// v_permlane32_swap per register then hands every lane both halves of its own group.
 constexpr int kRowsUnroll = 2;  // 16-element groups per lane, 64 groups apart
 
-template <bool F32>
-__device__ __forceinline__ void load16(const char *p, float *v)
+// 16 consecutive f32 values (f32 input keeps one lane's 64 bytes in four 16-byte loads)
+__device__ __forceinline__ void load16_f32(const char *p, float *v)
 {
-    if constexpr (F32) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(p + 16 * k);
-            v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
-        }
-    } else {
+    for (int k = 0; k < 4; ++k) {
+        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 16 * k));
+        v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
+    }
+}
+
+// (lo, hi) -> lanes 0-31 keep lo and take the lo of lanes 32-63; lanes 32-63 take the hi of
+// lanes 0-31 and keep hi: with lo = half h of group l % 32 and hi = half h of group 32 + l % 32
+// (h = l / 32), lane l ends with both halves of group l.
+__device__ __forceinline__ void pair_halves(u32x4 &lo, u32x4 &hi)
+{
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const u32x4 t = *reinterpret_cast<const u32x4 *>(p + 16 * k);
-            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+    for (int d = 0; d < 4; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+        lo[d] = r[0];
+        hi[d] = r[1];
+    }
+}
+
+__device__ __forceinline__ void unpack_bf16x16(const u32x4 &a, const u32x4 &b, float *v)
+{
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                v[8 * k + 2 * u] = bf16_lo(w[u]);
-                v[8 * k + 2 * u + 1] = bf16_hi(w[u]);
-            }
-        }
+    for (int u = 0; u < 8; ++u) {
+        v[2 * u] = bf16_lo(w[u]);
+        v[2 * u + 1] = bf16_hi(w[u]);
     }
 }
 
@@ -61,7 +74,7 @@ template <int H, bool F32, bool SR, bool TILED, bool RHT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const void *__restrict__ x, int64_t ldx, uint32_t groups_per_row, uint32_t total_groups,
     uint8_t *__restrict__ q, int64_t ldq, uint8_t *__restrict__ scales, int64_t lds, uint32_t key0,
-    uint32_t key1, uint32_t stream_id, int64_t L, uint32_t noclip, float norm)
+    uint32_t key1, uint32_t stream_id, int64_t L, uint32_t noclip, float norm, uint32_t last_row)
 {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t base = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * (64u * kRowsUnroll);
@@ -71,7 +84,46 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     float v[kRowsUnroll][16];
     uint32_t row[kRowsUnroll], grp[kRowsUnroll];
     bool live[kRowsUnroll];
-    {
+    if constexpr (!F32) {
+        // groups base + 64 u + (lane % 32) (A) and + 32 (B): their halves lane / 32 are loaded,
+        // then paired; a group past the end loads the last group instead and is not stored
+        const uint32_t half = lane >> 5, ml = lane & 31u;
+        uint32_t rA = (base + ml) / groups_per_row;
+        uint32_t cA = base + ml - rA * groups_per_row;
+        u32x4 lo[kRowsUnroll], hi[kRowsUnroll];
+#pragma unroll
+        for (int u = 0; u < kRowsUnroll; ++u) {
+            if (u > 0) {
+                cA += 64u;
+                while (cA >= groups_per_row) {
+                    cA -= groups_per_row;
+                    ++rA;
+                }
+            }
+            uint32_t rB = rA, cB = cA + 32u;
+            while (cB >= groups_per_row) {
+                cB -= groups_per_row;
+                ++rB;
+            }
+            const uint32_t gA = base + 64u * u + ml;
+            const bool liveA = gA < total_groups, liveB = gA + 32u < total_groups;
+            live[u] = half ? liveB : liveA;
+            row[u] = half ? rB : rA;
+            grp[u] = half ? cB : cA;
+            const uint32_t lrA = liveA ? rA : last_row, lcA = liveA ? cA : groups_per_row - 1u;
+            const uint32_t lrB = liveB ? rB : last_row, lcB = liveB ? cB : groups_per_row - 1u;
+            const uint16_t *xh = reinterpret_cast<const uint16_t *>(x);
+            const u32x4 *pa = reinterpret_cast<const u32x4 *>(xh + (int64_t)lrA * ldx + (int64_t)lcA * 16 + 8 * half);
+            const u32x4 *pb = reinterpret_cast<const u32x4 *>(xh + (int64_t)lrB * ldx + (int64_t)lcB * 16 + 8 * half);
+            lo[u] = __builtin_nontemporal_load(pa);
+            hi[u] = __builtin_nontemporal_load(pb);
+        }
+#pragma unroll
+        for (int u = 0; u < kRowsUnroll; ++u) {
+            pair_halves(lo[u], hi[u]);
+            unpack_bf16x16(lo[u], hi[u], v[u]);
+        }
+    } else {
         // every lane runs (the cross-lane steps need both lanes of a block); a group past the end
         // is replaced by one of the last block, same lane within the pair, and is not stored
         uint32_t g = base + lane;
@@ -101,8 +153,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
         // all loads in flight before any is consumed
 #pragma unroll
         for (int u = 0; u < kRowsUnroll; ++u)
-            load16<F32>(reinterpret_cast<const char *>(x) + ((int64_t)row[u] * ldx + (int64_t)grp[u] * 16) * esize,
-                        v[u]);
+            load16_f32(reinterpret_cast<const char *>(x) + ((int64_t)row[u] * ldx + (int64_t)grp[u] * 16) * esize, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kRowsUnroll; ++u) {
@@ -332,13 +383,29 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
         // the loads stay unconditional, and whatever it computes from them is never stored
         const uint32_t lg = min(gi, ncols / 16u - 1u);
         u32x4 raw[kSteps][kParts];
+        if constexpr (!F32) {
+            // coalesced: lane l loads half l / 32 of the group of lane l % 32 (rows 0-3 of the
+            // step) and of lane 32 + l % 32 (rows 4-7); a swap pairs the halves (quant_rows)
+            const uint32_t half = lane >> 5, ml = lane & 31u;
 #pragma unroll
-        for (int k = 0; k < kSteps; ++k) {
-            const uint32_t lr = min(32u * k + 8u * wave + lane / 8u, nrows - 1u);
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(xb + ((int64_t)(r0 + lr) * ldx + c0 + 16 * lg) * kEsize);
-            // plain loads: of a lane's 32 (64) bytes, the later 16-byte pieces come from L1
+            for (int k = 0; k < kSteps; ++k) {
+                const uint32_t lrA = min(32u * k + 8u * wave + ml / 8u, nrows - 1u);
+                const uint32_t lrB = min(32u * k + 8u * wave + 4u + ml / 8u, nrows - 1u);
+                const int64_t col = c0 + 16 * lg + 8 * half;
+                const uint16_t *xh = reinterpret_cast<const uint16_t *>(xb);
+                raw[k][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xh + (int64_t)(r0 + lrA) * ldx + col));
+                raw[k][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xh + (int64_t)(r0 + lrB) * ldx + col));
+            }
 #pragma unroll
-            for (int p = 0; p < kParts; ++p) raw[k][p] = src[p];
+            for (int k = 0; k < kSteps; ++k) pair_halves(raw[k][0], raw[k][1]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kSteps; ++k) {
+                const uint32_t lr = min(32u * k + 8u * wave + lane / 8u, nrows - 1u);
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(xb + ((int64_t)(r0 + lr) * ldx + c0 + 16 * lg) * 4);
+#pragma unroll
+                for (int p = 0; p < kParts; ++p) raw[k][p] = __builtin_nontemporal_load(src + p);
+            }
         }
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
@@ -512,7 +579,8 @@ hipError_t rows_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx,
     const uint32_t per_block = kThreads * kRowsUnroll;
     const dim3 grid((total + per_block - 1) / per_block);
     return launch(quant_rows_kernel<H, F32, SR, TILED, RHT>, grid, dim3(kThreads), 0, stream, x, ldx, gpr, total, q,
-                  ldq, scales, lds, (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, cols, noclip ? 1u : 0u, norm);
+                  ldq, scales, lds, (uint32_t)seed, (uint32_t)(seed >> 32), stream_id, cols, noclip ? 1u : 0u, norm,
+                  (uint32_t)(rows - 1));
 }
 
 template <int H, bool F32, bool SR, bool TILED, bool RHT>
