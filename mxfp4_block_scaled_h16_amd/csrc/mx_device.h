@@ -123,23 +123,24 @@ __device__ __forceinline__ float e8m0_reciprocal(uint32_t s)
 
 // Stochastic E2M1 magnitude index of a = |v| >= 0 with random word r: saturate at 6, else round
 // up to the next grid value iff r < 2^32 f, f = fractional position of a between its two grid
-// neighbours. Read from the bit pattern A of a:
-//  * a in [1, 6): the step is half the value's leading power of two, so the magnitude index of
+// neighbours. a is first clamped to 6 (6 is its own lower neighbour, index 7, with f = 0, so
+// everything from 6 up saturates; a NaN also lands there, in a block whose codes are discarded).
+// Then, from the bit pattern A of a:
+//  * a in [1, 6]: the step is half the value's leading power of two, so the magnitude index of
 //    the lower neighbour is 2 * (biased exponent) + (top mantissa bit) - 252 and 2^32 f is the
 //    remaining 22 mantissa bits, A << 10;
-//  * a in [1/2, 1): lower neighbour 1/2 (index 1), step 1/2, 2^32 f = the 23 mantissa bits, A << 9;
+//  * a in [1/2, 1): lower neighbour 1/2 (index 1; the formula above gives 0 or 1 there, hence
+//    the max), step 1/2, 2^32 f = the 23 mantissa bits, A << 9;
 //  * a < 1/2: lower neighbour 0, f = 2 a, and r < 2^33 a is r < ceil(2^33 a) (exact products).
 __device__ __forceinline__ uint32_t e2m1_stochastic(float a, uint32_t r)
 {
+    a = fminf(a, 6.0f);
     const uint32_t A = __float_as_uint(a);
     const bool ge1 = A >= 0x3F800000u, ge_half = A >= 0x3F000000u;
     const uint32_t t_small = (uint32_t)ceilf(a * 8589934592.0f);
-    const uint32_t lo = ge1 ? (A >> 22) - 252u : (ge_half ? 1u : 0u);
-    const uint32_t t = ge1 ? (A << 10) : (ge_half ? (A << 9) : t_small);
-    const uint32_t mag = lo + (r < t ? 1u : 0u);
-    // the block scale keeps a below 8, so a in [6, 8) has lo = 7 and saturates here (a NaN or
-    // infinity also lands on 7, in a block whose codes are discarded)
-    return min(mag, 7u);
+    const uint32_t lo = ge_half ? max((A >> 22) - 252u, 1u) : 0u;
+    const uint32_t t = ge_half ? A << (ge1 ? 10u : 9u) : t_small;
+    return lo + (r < t ? 1u : 0u);
 }
 
 
