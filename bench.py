@@ -498,6 +498,45 @@ def machine_ceilings(settle_s=0.25, reps=10):
     return out
 
 
+def step_entry_points(plan, steps, warmup, settle_s=0.25):
+    """The same step through the library's training-step calls (mxfp4_linear_forward, then
+    mxfp4_linear_backward: X, W and dY each quantized once along both axes, three GEMMs), on the
+    plan's inputs, workspaces allocated once outside the timed region. Host clock over K steps."""
+    import torch
+    mx = plan.mx
+    if plan.passes != "FDW" or len(plan.projs) != 1:
+        return None
+    name, K, N = plan.projs[0]
+    M = plan.M
+    ws = torch.empty(mx.step_workspace_bytes(M, K, N), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    dx = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        d_acts, d_proj = plan.sets[i % len(plan.sets)]
+        x = d_acts[next(iter(d_acts))]
+        w, dy = d_proj[name]
+        mx.linear_forward(x, w, plan.h, "rne", "rne", "sr", 0x5EED, workspace=ws, out=y)
+        mx.linear_backward(dy, K, ws, plan.h, "rne", "rne", "sr", 0x5EED, dx=dx, dw=dw)
+    t_end, i = time.perf_counter() + settle_s, 0
+    while time.perf_counter() < t_end:
+        step(i)
+        i += 1
+        torch.cuda.synchronize()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flops = 3 * 2.0 * M * N * K
+    return {"calls": "mxfp4_linear_forward + mxfp4_linear_backward", "ms_per_step": round(ms, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+
+
 def library_baselines(M, N, K, steps, settle_s=0.25):
     """Vendor GEMMs (hipBLASLt through torch._scaled_mm / torch.mm) at one product shape, as
     context: block-scaled MXFP8 and MXFP4 (E8M0 scale per 32 along K), per-tensor FP8 and
@@ -616,6 +655,8 @@ def main():
                  "launches": [label for label, _, _, _ in fplan.op_list]}
         del fplan
 
+    entry = step_entry_points(plan, args.steps, args.warmup) if args.workload == "qkv" else None
+
     baselines = None
     if args.workload == "qkv" and not args.no_library_baselines:
         baselines = library_baselines(M, projs[0][2], projs[0][1], args.steps)
@@ -658,6 +699,8 @@ def main():
     if fprop is not None:
         line["fprop_only"] = fprop
     line["quantization_error"] = qerr
+    if entry is not None:
+        line["step_entry_points"] = entry
     if ceilings is not None:
         line["ceilings"] = ceilings
     if baselines is not None:

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 7
+#define MXFP4_ABI_VERSION 8
 
 typedef enum {
     MXFP4_OK = 0,
@@ -269,6 +269,41 @@ mxfp4_status_t mxfp4_linear_dgrad(const void *dy_bf16, const void *w_bf16, int64
 mxfp4_status_t mxfp4_linear_wgrad(const void *dy_bf16, const void *x_bf16, int64_t M, int64_t K,
                                   int64_t N, const mxfp4_linear_cfg_t *cfg, void *ws,
                                   size_t ws_bytes, float *dw, void *stream);
+
+/*
+ * One training step of the linear layer, split where a training loop splits it: the forward
+ * call needs X and W, the backward call dY. Each of X, W and dY is read and quantized ONCE, along
+ * both of its axes (the one-pass quantizer of mxfp4_quantize_dual), instead of once per GEMM:
+ *   mxfp4_linear_forward : X along K (Fprop) and along M (Wgrad), W along K (Fprop) and along N
+ *                          (Dgrad); writes y[M][N] = Fprop and keeps the four quantizations in ws;
+ *   mxfp4_linear_backward: dY along N (Dgrad) and along M (Wgrad); writes dx[M][K] = Dgrad and
+ *                          dw[N][K] = Wgrad from the operands the forward call left in ws.
+ * Roundings are per product, for both of its operands; Philox streams and keys are those of the
+ * separate calls (stream 0 = first operand, 1 = second, key = seed), so y, dx and dw are
+ * bitwise those of mxfp4_linear_fprop / _dgrad / _wgrad with cfg {hadamard, r, r, seed} and
+ * r = fprop, dgrad, wgrad respectively.
+ * Requirements: M, K and N are all contraction lengths here, so each must be a multiple of 32.
+ * Inputs bf16 dense row-major, 16-byte aligned; outputs FP32 dense row-major, 4-byte aligned.
+ * ws: at least mxfp4_linear_step_workspace_bytes(M, K, N) device bytes, 256-byte aligned; the
+ * backward call must get the same ws, unchanged since the forward call of the same step (calls
+ * on one stream are ordered; across streams the caller orders them). Errors as elsewhere:
+ * MXFP4_ERR_WORKSPACE for a short ws, nothing launched on any argument error.
+ */
+typedef struct {
+    int hadamard;              /* as in mxfp4_linear_cfg_t */
+    mxfp4_rounding_t fprop;    /* X along K and W along K */
+    mxfp4_rounding_t dgrad;    /* dY along N and W along N */
+    mxfp4_rounding_t wgrad;    /* dY along M and X along M */
+    uint64_t seed;             /* Philox key of every stochastic rounding of the step */
+} mxfp4_step_cfg_t;
+
+size_t mxfp4_linear_step_workspace_bytes(int64_t M, int64_t K, int64_t N);
+mxfp4_status_t mxfp4_linear_forward(const void *x_bf16, const void *w_bf16, int64_t M, int64_t K,
+                                    int64_t N, const mxfp4_step_cfg_t *cfg, void *ws,
+                                    size_t ws_bytes, float *y, void *stream);
+mxfp4_status_t mxfp4_linear_backward(const void *dy_bf16, int64_t M, int64_t K, int64_t N,
+                                     const mxfp4_step_cfg_t *cfg, void *ws, size_t ws_bytes,
+                                     float *dx, float *dw, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *mxfp4_status_string(mxfp4_status_t status);

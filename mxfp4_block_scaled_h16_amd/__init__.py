@@ -15,7 +15,7 @@ import torch  # imported first: the library binds to the HIP runtime torch has l
 
 __all__ = [
     "Mxfp4Error", "RHT", "ORTHO", "SCALE_NOCLIP", "quantize", "quantize_dual", "gemm", "linear_fprop",
-    "linear_dgrad", "linear_wgrad", "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD", "ROWS", "TILED",
+    "linear_dgrad", "linear_wgrad", "linear_forward", "linear_backward", "step_workspace_bytes", "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD", "ROWS", "TILED",
     "tiled_sizes", "gemm_workspace_bytes",
 ]
 
@@ -49,6 +49,12 @@ class QuantOut(ctypes.Structure):
 class LinearCfg(ctypes.Structure):
     _fields_ = [("hadamard", ctypes.c_int), ("rnd_a", ctypes.c_int), ("rnd_b", ctypes.c_int),
                 ("seed", ctypes.c_uint64)]
+
+
+class StepCfg(ctypes.Structure):
+    """mxfp4_step_cfg_t: rotation, per-product roundings and the Philox key of a training step."""
+    _fields_ = [("hadamard", ctypes.c_int), ("fprop", ctypes.c_int), ("dgrad", ctypes.c_int),
+                ("wgrad", ctypes.c_int), ("seed", ctypes.c_uint64)]
 
 
 def library_path() -> str:
@@ -86,6 +92,13 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [vp, vp, i64, i64, i64, ctypes.POINTER(LinearCfg), vp, ctypes.c_size_t, vp, vp]
         f.restype = ci
+    L.mxfp4_linear_step_workspace_bytes.argtypes = [i64, i64, i64]
+    L.mxfp4_linear_step_workspace_bytes.restype = ctypes.c_size_t
+    L.mxfp4_linear_forward.argtypes = [vp, vp, i64, i64, i64, ctypes.POINTER(StepCfg), vp, ctypes.c_size_t, vp, vp]
+    L.mxfp4_linear_forward.restype = ci
+    L.mxfp4_linear_backward.argtypes = [vp, i64, i64, i64, ctypes.POINTER(StepCfg), vp, ctypes.c_size_t, vp, vp,
+                                        vp]
+    L.mxfp4_linear_backward.restype = ci
     L.mxfp4_status_string.argtypes = [ci]
     L.mxfp4_status_string.restype = ctypes.c_char_p
     L.mxfp4_abi_version.argtypes = []
@@ -315,3 +328,54 @@ def linear_wgrad(dy, x, hadamard=16, rnd_a="rne", rnd_b="rne", seed=0, out=None,
     K = x.shape[1]
     return _linear("mxfp4_linear_wgrad", WGRAD, dy, x, M, K, N, (N, K), hadamard, rnd_a, rnd_b,
                    seed, out, workspace, stream)
+
+
+def step_workspace_bytes(M, K, N) -> int:
+    return int(lib().mxfp4_linear_step_workspace_bytes(int(M), int(K), int(N)))
+
+
+def _step_cfg(hadamard, fprop, dgrad, wgrad, seed):
+    return StepCfg(int(hadamard), _rounding(fprop), _rounding(dgrad), _rounding(wgrad), int(seed) & (2 ** 64 - 1))
+
+
+def linear_forward(x, w, hadamard=16, fprop="rne", dgrad="rne", wgrad="sr", seed=0, workspace=None, out=None,
+                   stream=None):
+    """Forward half of a training step: Y[M,N] = X W^T, with X and W each quantized once along
+    both axes; the axes the backward products need stay in `workspace`. Returns (Y, workspace);
+    pass the same workspace, unchanged, to linear_backward of the same step."""
+    for t, name in ((x, "x"), (w, "w")):
+        _require_cuda(t, name)
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError("%s must be contiguous bfloat16" % name)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w disagree on K")
+    if workspace is None:
+        workspace = torch.empty(max(step_workspace_bytes(M, K, N), 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    cfg = _step_cfg(hadamard, fprop, dgrad, wgrad, seed)
+    st = lib().mxfp4_linear_forward(x.data_ptr(), w.data_ptr(), M, K, N, ctypes.byref(cfg), workspace.data_ptr(),
+                                    workspace.numel(), out.data_ptr(), _stream(stream))
+    _check(st, "mxfp4_linear_forward")
+    return out, workspace
+
+
+def linear_backward(dy, K, workspace, hadamard=16, fprop="rne", dgrad="rne", wgrad="sr", seed=0, dx=None,
+                    dw=None, stream=None):
+    """Backward half of a training step: dX[M,K] = dY W and dW[N,K] = dY^T X from dY[M,N] and the
+    workspace of the step's linear_forward call (same configuration). Returns (dX, dW)."""
+    _require_cuda(dy, "dy")
+    if dy.dtype != torch.bfloat16 or not dy.is_contiguous():
+        raise TypeError("dy must be contiguous bfloat16")
+    M, N = dy.shape
+    if dx is None:
+        dx = torch.empty((M, int(K)), dtype=torch.float32, device=dy.device)
+    if dw is None:
+        dw = torch.empty((N, int(K)), dtype=torch.float32, device=dy.device)
+    cfg = _step_cfg(hadamard, fprop, dgrad, wgrad, seed)
+    st = lib().mxfp4_linear_backward(dy.data_ptr(), M, int(K), N, ctypes.byref(cfg), workspace.data_ptr(),
+                                     workspace.numel(), dx.data_ptr(), dw.data_ptr(), _stream(stream))
+    _check(st, "mxfp4_linear_backward")
+    return dx, dw

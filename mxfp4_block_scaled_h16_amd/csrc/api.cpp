@@ -1,6 +1,7 @@
 // C-ABI entry points: argument validation, workspace carve-up and kernel dispatch.
 // Every argument check happens before the first HIP call, so an invalid call launches nothing,
 // touches no output and needs no device.
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cstdint>
@@ -208,6 +209,91 @@ mxfp4_status_t run_linear(const LinearSpec &sp, mxfp4_pass_t pass, int64_t M, in
     return from_hip(e);
 }
 
+// ---------------------------------------------------------------- training step ----------
+// Workspace of one step: X, W and dY quantized along both axes, each laid out as the separate
+// linear calls lay it out (tiled when its quantized length is a multiple of 512), then the
+// split-K partials of the largest of the three products (the products run one after another).
+enum { kXr, kWr, kXc, kWc, kDYr, kDYc, kStepOperands };
+
+struct StepSpace {
+    OperandSpace op[kStepOperands];
+    size_t off[kStepOperands];  // codes at off, scales at off + round256(codes)
+    size_t splitk_off, total;
+};
+
+StepSpace step_space(int64_t M, int64_t K, int64_t N)
+{
+    StepSpace sp;
+    sp.op[kXr] = {M, K};   // X along K: Fprop A
+    sp.op[kWr] = {N, K};   // W along K: Fprop B
+    sp.op[kXc] = {K, M};   // X along M: Wgrad B
+    sp.op[kWc] = {K, N};   // W along N: Dgrad B
+    sp.op[kDYr] = {M, N};  // dY along N: Dgrad A
+    sp.op[kDYc] = {N, M};  // dY along M: Wgrad A
+    size_t o = 0;
+    for (int i = 0; i < kStepOperands; ++i) {
+        sp.off[i] = o;
+        o += round256(sp.op[i].codes()) + round256(sp.op[i].scales());
+    }
+    sp.splitk_off = o;
+    size_t sk = mx::gemm_workspace_bytes(M, N, K);
+    sk = std::max(sk, mx::gemm_workspace_bytes(M, K, N));
+    sk = std::max(sk, mx::gemm_workspace_bytes(N, K, M));
+    sp.total = o + round256(sk);
+    return sp;
+}
+
+mxfp4_status_t check_step(int64_t M, int64_t K, int64_t N, const mxfp4_step_cfg_t *cfg, const void *ws,
+                          size_t ws_bytes, StepSpace *sp)
+{
+    if (!cfg) return MXFP4_ERR_NULL;
+    if (M < 0 || K < 0 || N < 0 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return MXFP4_ERR_SHAPE;
+    if (M % 32 != 0 || K % 32 != 0 || N % 32 != 0) return MXFP4_ERR_SHAPE;
+    if (!valid_rotation(cfg->hadamard)) return MXFP4_ERR_ARG;
+    if (!valid_rounding(cfg->fprop) || !valid_rounding(cfg->dgrad) || !valid_rounding(cfg->wgrad))
+        return MXFP4_ERR_ARG;
+    *sp = step_space(M, K, N);
+    for (const OperandSpace &o : sp->op) {
+        if (o.L / 32 > 0 && o.outer > kMaxBlocks / (o.L / 32)) return MXFP4_ERR_SHAPE;
+        if (o.tiled() && o.codes() > UINT32_MAX) return MXFP4_ERR_SHAPE;
+    }
+    if (ws_bytes < sp->total || (sp->total > 0 && !ws)) return MXFP4_ERR_WORKSPACE;
+    if (ws && !aligned(ws, 256)) return MXFP4_ERR_ALIGN;
+    return MXFP4_OK;
+}
+
+float step_alpha(int hadamard)
+{
+    const int h = hadamard & ~(MXFP4_RHT | MXFP4_ORTHONORMAL);
+    return (hadamard & MXFP4_ORTHONORMAL) || h == 0 ? 1.0f : 1.0f / (float)h;
+}
+
+// one output of a step's dual quantization, into the workspace
+mx::QuantOut step_out(const StepSpace &sp, int which, uint8_t *ws, mxfp4_rounding_t rnd, uint64_t seed,
+                      uint32_t stream_id)
+{
+    const OperandSpace &o = sp.op[which];
+    uint8_t *q = ws + sp.off[which];
+    return mx::QuantOut{is_sr(rnd), is_noclip(rnd), seed, stream_id, o.tiled(), q, o.L / 2,
+                        q + round256(o.codes()), o.L / 32};
+}
+
+// out[rows][cols] = alpha A B^T over the contraction of operands a, b of the workspace (zero for
+// an empty contraction)
+hipError_t step_gemm(const StepSpace &sp, int a, int b, uint8_t *ws, size_t ws_bytes, int64_t rows, int64_t cols,
+                     float alpha, float *out, hipStream_t s)
+{
+    const OperandSpace &oa = sp.op[a], &ob = sp.op[b];
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (oa.L == 0) return mx::launch_empty_product(out, false, rows, cols, cols, 0.0f, s);
+    const uint8_t *aq = ws + sp.off[a], *bq = ws + sp.off[b];
+    return mx::launch_gemm(aq, oa.L / 2, aq + round256(oa.codes()), oa.L / 32, bq, ob.L / 2,
+                           bq + round256(ob.codes()), ob.L / 32, rows, cols, oa.L, alpha, 0.0f, out, false, cols,
+                           oa.tiled(), ws + sp.splitk_off, ws_bytes - sp.splitk_off, s);
+}
+
+bool input_ok(const void *p) { return p != nullptr && aligned(p, 16); }
+
 }  // namespace
 
 extern "C" {
@@ -335,6 +421,66 @@ mxfp4_status_t mxfp4_linear_wgrad(const void *dy_bf16, const void *x_bf16, int64
 {
     LinearSpec sp{dy_bf16, M, N, 0, x_bf16, M, K, 0, N, K, M};
     return run_linear(sp, MXFP4_WGRAD, M, K, N, cfg, ws, ws_bytes, dw, stream);
+}
+
+size_t mxfp4_linear_step_workspace_bytes(int64_t M, int64_t K, int64_t N)
+{
+    if (M < 0 || K < 0 || N < 0 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return 0;
+    return step_space(M, K, N).total;
+}
+
+mxfp4_status_t mxfp4_linear_forward(const void *x_bf16, const void *w_bf16, int64_t M, int64_t K,
+                                    int64_t N, const mxfp4_step_cfg_t *cfg, void *ws,
+                                    size_t ws_bytes, float *y, void *stream)
+{
+    StepSpace sp;
+    if (mxfp4_status_t st = check_step(M, K, N, cfg, ws, ws_bytes, &sp)) return st;
+    const bool need_x = M > 0 && K > 0, need_w = N > 0 && K > 0, need_y = M > 0 && N > 0;
+    if ((need_x && !x_bf16) || (need_w && !w_bf16) || (need_y && !y)) return MXFP4_ERR_NULL;
+    if ((need_x && !input_ok(x_bf16)) || (need_w && !input_ok(w_bf16)) || (need_y && !aligned(y, 4)))
+        return MXFP4_ERR_ALIGN;
+    if (!need_x && !need_w && !need_y) return MXFP4_OK;
+    if (mxfp4_status_t st = check_device()) return st;
+    uint8_t *p = static_cast<uint8_t *>(ws);
+    hipStream_t s = (hipStream_t)stream;
+    const uint64_t seed = cfg->seed;
+    hipError_t e = hipSuccess;
+    // X: along K for Fprop (first operand, stream 0), along M for Wgrad (second operand, stream 1)
+    if (need_x)
+        e = mx::launch_quantize_dual(x_bf16, false, M, K, K, cfg->hadamard, step_out(sp, kXr, p, cfg->fprop, seed, 0u),
+                                     step_out(sp, kXc, p, cfg->wgrad, seed, 1u), s);
+    // W: along K for Fprop, along N for Dgrad (second operand of both, stream 1)
+    if (e == hipSuccess && need_w)
+        e = mx::launch_quantize_dual(w_bf16, false, N, K, K, cfg->hadamard, step_out(sp, kWr, p, cfg->fprop, seed, 1u),
+                                     step_out(sp, kWc, p, cfg->dgrad, seed, 1u), s);
+    if (e == hipSuccess) e = step_gemm(sp, kXr, kWr, p, ws_bytes, M, N, step_alpha(cfg->hadamard), y, s);
+    return from_hip(e);
+}
+
+mxfp4_status_t mxfp4_linear_backward(const void *dy_bf16, int64_t M, int64_t K, int64_t N,
+                                     const mxfp4_step_cfg_t *cfg, void *ws, size_t ws_bytes,
+                                     float *dx, float *dw, void *stream)
+{
+    StepSpace sp;
+    if (mxfp4_status_t st = check_step(M, K, N, cfg, ws, ws_bytes, &sp)) return st;
+    const bool need_dy = M > 0 && N > 0, need_dx = M > 0 && K > 0, need_dw = N > 0 && K > 0;
+    if ((need_dy && !dy_bf16) || (need_dx && !dx) || (need_dw && !dw)) return MXFP4_ERR_NULL;
+    if ((need_dy && !input_ok(dy_bf16)) || (need_dx && !aligned(dx, 4)) || (need_dw && !aligned(dw, 4)))
+        return MXFP4_ERR_ALIGN;
+    if (!need_dy && !need_dx && !need_dw) return MXFP4_OK;
+    if (mxfp4_status_t st = check_device()) return st;
+    uint8_t *p = static_cast<uint8_t *>(ws);
+    hipStream_t s = (hipStream_t)stream;
+    const float alpha = step_alpha(cfg->hadamard);
+    hipError_t e = hipSuccess;
+    // dY: along N for Dgrad, along M for Wgrad (first operand of both, stream 0)
+    if (need_dy)
+        e = mx::launch_quantize_dual(dy_bf16, false, M, N, N, cfg->hadamard,
+                                     step_out(sp, kDYr, p, cfg->dgrad, cfg->seed, 0u),
+                                     step_out(sp, kDYc, p, cfg->wgrad, cfg->seed, 0u), s);
+    if (e == hipSuccess) e = step_gemm(sp, kDYr, kWc, p, ws_bytes, M, K, alpha, dx, s);
+    if (e == hipSuccess) e = step_gemm(sp, kDYc, kXc, p, ws_bytes, N, K, alpha, dw, s);
+    return from_hip(e);
 }
 
 const char *mxfp4_status_string(mxfp4_status_t status)

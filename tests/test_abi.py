@@ -32,6 +32,7 @@ def test_header_declares_the_boundary():
         assert expected in names
     assert "mxfp4_tiled_sizes" in names and "mxfp4_gemm_workspace_bytes" in names
     assert "mxfp4_quantize_dual" in names
+    assert {"mxfp4_linear_forward", "mxfp4_linear_backward", "mxfp4_linear_step_workspace_bytes"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -62,7 +63,7 @@ def test_ceiling_library_exports_its_declared_symbols():
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 7
+    assert L.mxfp4_abi_version() == 8
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -232,3 +233,30 @@ def test_gemm_ex_argument_errors(L):
     assert g(c=None) == 1
     assert g(ldc=32) == 3                     # ldc < N
     assert g(M=0) == 0 and g(M=0, c=None) == 0
+
+
+def test_step_argument_errors(L):
+    """The training-step calls validate before any launch: every size a multiple of 32 (all three
+    are contractions of the step), roundings and rotation as elsewhere, the workspace size and
+    alignment; all-empty steps succeed without a device call."""
+    import mxfp4_block_scaled_h16_amd as mx
+    ok = mx.StepCfg(16, 0, 0, 1, 7)
+    f, b = L.mxfp4_linear_forward, L.mxfp4_linear_backward
+    ws = mx.step_workspace_bytes(64, 64, 64)
+    assert ws >= 3 * mx.workspace_bytes(mx.FPROP, 64, 64, 64) // 2 > 0
+    assert mx.step_workspace_bytes(-1, 64, 64) == 0 and mx.step_workspace_bytes(0, 0, 0) == 0
+    buf = 1 << 12
+    assert f(buf, buf, 64, 64, 64, None, buf, ws, buf, None) == 1
+    assert f(buf, buf, 48, 64, 64, ctypes.byref(ok), buf, ws, buf, None) == 2     # M % 32
+    assert b(buf, 64, 64, 40, ctypes.byref(ok), buf, 1 << 30, buf, buf, None) == 2  # N % 32
+    assert f(buf, buf, 64, 64, 64, ctypes.byref(mx.StepCfg(12, 0, 0, 0, 0)), buf, ws, buf, None) == 3
+    assert f(buf, buf, 64, 64, 64, ctypes.byref(mx.StepCfg(16, 0, 5, 0, 0)), buf, ws, buf, None) == 3
+    assert f(buf, buf, 64, 64, 64, ctypes.byref(ok), buf, ws - 1, buf, None) == 5
+    assert f(buf, buf, 64, 64, 64, ctypes.byref(ok), None, ws, buf, None) == 5
+    assert f(buf, buf, 64, 64, 64, ctypes.byref(ok), buf + 16, ws, buf, None) == 4   # ws 256-byte aligned
+    assert f(None, buf, 64, 64, 64, ctypes.byref(ok), buf, ws, buf, None) == 1
+    assert f(buf + 2, buf, 64, 64, 64, ctypes.byref(ok), buf, ws, buf, None) == 4
+    assert b(buf, 64, 64, 64, ctypes.byref(ok), buf, ws, None, buf, None) == 1
+    assert f(None, None, 0, 0, 0, ctypes.byref(ok), None, 0, None, None) == 0
+    assert b(None, 0, 0, 0, ctypes.byref(ok), None, 0, None, None, None) == 0
+
