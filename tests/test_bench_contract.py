@@ -1,0 +1,26 @@
+"""Host-side parts of the benchmark contract that need no GPU: one GPU only (a multi-GPU request
+exits with a message and status 2, before anything touches a device), and the workloads and
+byte counts the benchmark's figures are computed from."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_workloads_name_their_shapes():
+    sys.path.insert(0, ROOT)
+    import bench
+    desc, projs, passes, M = bench.WORKLOADS["qkv"]
+    assert (projs, passes, M) == ([("qkv", 4096, 6144)], "FDW", 8192)
+    assert bench.WORKLOADS["layer"][1] == bench.LLAMA_PROJ and len(bench.LLAMA_PROJ) == 7
+    assert bench.DUAL_BYTES_PER_ELEM == 2 + 2 * (0.5 + 1 / 32)
+    assert bench.QUANT_BYTES_PER_ELEM == 2 + 0.5 + 1 / 32
