@@ -1,7 +1,8 @@
 """Pins of the CPU oracle to facts outside itself (no GPU needed).
 
 Each test checks the oracle against something it does not compute itself: a library routine
-(scipy's Hadamard, numpy's Philox, torch's E8M0 decode), a closed form, a hand-derived table in
+(scipy's Hadamard, numpy's Philox, torch's E8M0 decode, the published Philox4x32-10
+known answers), a closed form, a hand-derived table in
 tests/golden/, exact rational brute force (oracle.exact), or an exact construction whose answer
 is a plain matrix product. A plausible slip in the oracle (a dropped stage, a swapped sign or
 index, a transposed operand, a wrong tie rule) fails at least one of them.
@@ -282,6 +283,18 @@ def test_philox_weyl_constants_closed_form():
         _, _, w0, w1 = exact.PHILOX_CONSTANTS[width]
         assert w0 == exact.weyl_constant(width, "phi")
         assert w1 == exact.weyl_constant(width, "sqrt3")
+
+
+def test_philox4x32_10_known_answers():
+    """The 32-bit generator the stochastic rounding and the randomized signs draw from
+    reproduces the published Philox4x32-10 known-answer vectors (tests/golden)."""
+    rows = read_golden("philox4x32_10_kat.txt")
+    assert len(rows) == 3
+    for row in rows:
+        v = [int(t, 16) for t in row]
+        ctr, key, want = v[0:4], v[4:6], v[6:10]
+        assert [int(w) for w in oracle.philox4x32_10(ctr, key)] == want
+        assert exact.philox(ctr, key, 32) == want
 
 
 def test_philox4x32_oracle_matches_generic():
