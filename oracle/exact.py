@@ -34,7 +34,7 @@ def round_e2m1_stochastic(v: Fraction, r: int) -> int:
     """Magnitude index after stochastic rounding with the 32-bit word r.
 
     |v| >= 6 saturates; otherwise |v| lies in [lo, hi) between two neighbouring grid values and
-    rounds to hi exactly when r < 2^32 (|v| - lo) / (hi - lo).
+    rounds to hi exactly when floor(r / 2^10) < floor(2^22 (|v| - lo) / (hi - lo)).
     """
     a = abs(v)
     if a >= 6:
@@ -43,7 +43,7 @@ def round_e2m1_stochastic(v: Fraction, r: int) -> int:
         lo, hi = E2M1_GRID[idx], E2M1_GRID[idx + 1]
         if lo <= a < hi:
             f = (a - lo) / (hi - lo)
-            return idx + 1 if r < f * 2 ** 32 else idx
+            return idx + 1 if (r >> 10) < math.floor(f * 2 ** 22) else idx
     raise AssertionError("unreachable")
 
 

@@ -320,30 +320,33 @@ def test_sr_against_brute_force():
             assert codes[o, j] == ((8 if x[o, j] < 0 else 0) | mag)
 
 
-def test_sr_threshold_equality_rounds_down():
-    """Values with f * 2^32 equal to the element's random word r exactly: r < f 2^32 is false,
-    so they must round down (to 0); one more unit of f makes them round up (to 0.5)."""
+def test_sr_threshold_22_bits():
+    """The rounding decision compares the top 22 bits of the element's random word r with the
+    fractional position f truncated to 22 bits. With r a multiple of 2^10 and |v| = (r + d) 2^-33
+    (grid step 1/2 below 1/2, so f = (r + d) 2^-32 exactly): d = 0 (equality) rounds down, d = 512
+    (below the next 22-bit unit of f, truncated away) rounds down, d = 1024 (one unit more) rounds
+    up to 0.5."""
     seed, stream = 2024, 0
-    nblk = 3000
+    nblk = 8000
     x = np.zeros((nblk, 32), dtype=np.float32)
     x[:, 0] = 4.0
     picked = []
     for o in range(nblk):
         for j in range(1, 32):
             r = exact.sr_word(seed, stream, o * 32 + j)
-            if r & 0xFF == 0 and r:
+            if r & 0x3FF == 0 and 0 < r < 2 ** 32 - 1024:
                 picked.append((o, j, r))
-    assert len(picked) > 100
+    assert len(picked) > 150
+    offsets = (0, 512, 1024)
     for idx, (o, j, r) in enumerate(picked):
-        # |v| = r 2^-33 < 0.5 (grid step 0.5, lo = 0) gives f = r 2^-32 exactly
-        extra = 0 if idx % 2 == 0 else 1
-        x[o, j] = np.float32((r + extra * 256) * 2.0 ** -33)
-        assert float(x[o, j]) == (r + extra * 256) * 2.0 ** -33
+        d = offsets[idx % 3]
+        x[o, j] = np.float32((r + d) * 2.0 ** -33)
+        assert float(x[o, j]) == (r + d) * 2.0 ** -33
     q, s = oracle.quantize(x, axis=1, hadamard=0, rounding=1, seed=seed, stream=stream)
     codes = unpack_codes(q)
     for idx, (o, j, r) in enumerate(picked):
         expect = exact.round_e2m1_stochastic(Fraction(float(x[o, j])), r)
-        assert expect == (0 if idx % 2 == 0 else 1)
+        assert expect == (1 if idx % 3 == 2 else 0)
         assert codes[o, j] == expect
 
 
