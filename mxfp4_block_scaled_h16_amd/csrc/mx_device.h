@@ -114,36 +114,6 @@ __device__ __forceinline__ void prescale_if_zero_scale(float *v, uint32_t s)
     }
 }
 
-// 2^(127 - S) as binary32 multiplier for S in [0, 253] (exponent field 254 - S in [1, 254]).
-__device__ __forceinline__ float e8m0_reciprocal(uint32_t s)
-{
-    const uint32_t sc = s < 253u ? s : 253u;
-    return __uint_as_float((254u - sc) << 23);
-}
-
-// Stochastic E2M1 magnitude index of a = |v| >= 0 with random word r: saturate at 6, else round
-// up to the next grid value iff r < 2^32 f, f = fractional position of a between its two grid
-// neighbours. a is first clamped to 6 (6 is its own lower neighbour, index 7, with f = 0, so
-// everything from 6 up saturates; a NaN also lands there, in a block whose codes are discarded).
-// Then, from the bit pattern A of a:
-//  * a in [1, 6]: the step is half the value's leading power of two, so the magnitude index of
-//    the lower neighbour is 2 * (biased exponent) + (top mantissa bit) - 252 and 2^32 f is the
-//    remaining 22 mantissa bits, A << 10;
-//  * a in [1/2, 1): lower neighbour 1/2 (index 1; the formula above gives 0 or 1 there, hence
-//    the max), step 1/2, 2^32 f = the 23 mantissa bits, A << 9;
-//  * a < 1/2: lower neighbour 0, f = 2 a, and r < 2^33 a is r < ceil(2^33 a) (exact products).
-__device__ __forceinline__ uint32_t e2m1_stochastic(float a, uint32_t r)
-{
-    a = fminf(a, 6.0f);
-    const uint32_t A = __float_as_uint(a);
-    const bool ge1 = A >= 0x3F800000u, ge_half = A >= 0x3F000000u;
-    const uint32_t t_small = (uint32_t)ceilf(a * 8589934592.0f);
-    const uint32_t lo = ge_half ? max((A >> 22) - 252u, 1u) : 0u;
-    const uint32_t t = ge_half ? A << (ge1 ? 10u : 9u) : t_small;
-    return lo + (r < t ? 1u : 0u);
-}
-
-
 // ---------------------------------------------------------------------------- Philox4x32-10 --
 // Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten rounds;
 // each multiplies words 0 and 2 by fixed odd constants, swaps the halves of the products in and
@@ -199,26 +169,46 @@ __device__ __forceinline__ void apply_signs(float *v, uint32_t bits)
 }
 
 // ---------------------------------------------------------------------------- stochastic -----
-// Stochastic codes of 8 consecutive values y[0..7] (not yet scaled) whose first element has
-// position index0 (a multiple of 8) in the quantized output: two Philox blocks, word k of
-// block (index0 / 4 + b) for element 4 b + k.
-__device__ __forceinline__ uint32_t encode8_stochastic(const float *y, uint32_t s, uint64_t index0,
+// Stochastic codes of 8 consecutive values y[0..7] (block scale byte S, values already
+// pre-doubled when S = 0, divisor = e8m0_divisor(S)) whose first element has position index0 (a
+// multiple of 8) in the quantized output: word k of Philox block (index0 / 4 + b) for element
+// 4 b + k.
+//
+// gfx950's v_cvt_scalef32_sr_pk_fp4_f32 divides a pair of binary32 values by the scale and
+// rounds each to E2M1 stochastically, saturating at 6 and keeping the sign of the value (also
+// for zero results). For the first value of the pair and random operand u it rounds the
+// magnitude up iff u plus the value's fractional position between its two grid neighbours,
+// truncated to 22 bits and aligned to the top of the word, carries out of 32 bits; with
+// u = ~r that is floor(r / 2^10) < floor(2^22 f), the rounding rule defined above. The second
+// value of a pair would draw from a shifted copy of the same operand, so each instruction
+// converts one element, with partner 0.0 (which encodes as +0 and never rounds up): byte 0 of
+// the result holds the element's code in its low nibble and 0 above it. Only that byte is
+// defined (the compiler does not carry the other bytes of the destination through), so pairs
+// are merged with a shift and the four valid bytes gathered with byte permutes.
+
+// the code of y in bits 0-3 and 0 in bits 4-7; bits 8-31 undefined
+__device__ __forceinline__ uint32_t sr_fp4_byte0(float y, uint32_t r, float divisor)
+{
+    const f32x2 pair = {y, 0.0f};
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, ~r, divisor, 0);
+}
+
+__device__ __forceinline__ uint32_t encode8_stochastic(const float *y, float divisor, uint64_t index0,
                                                        uint32_t key0, uint32_t key1, uint32_t stream_id)
 {
-    const float mul = e8m0_reciprocal(s);
     const uint64_t c = index0 >> 2;
     const Philox4 r0 = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), stream_id, 0u, key0, key1);
     const uint64_t c1 = c + 1;
     const Philox4 r1 = philox4x32_10((uint32_t)c1, (uint32_t)(c1 >> 32), stream_id, 0u, key0, key1);
-    uint32_t word = 0u, signs = 0u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t rnd = e < 4 ? r0.w[e] : r1.w[e - 4];
-        word |= e2m1_stochastic(fabsf(y[e] * mul), rnd) << (4 * e);
-        // sign bit of y[e] to bit 4 e + 3 (the sign of the rotated value, also for zeros)
-        signs |= (__float_as_uint(y[e]) >> (28 - 4 * e)) & (8u << (4 * e));
-    }
-    return word | signs;
+    // byte 0 of p_k = codes of elements 2k (low nibble) and 2k + 1 (high nibble)
+    const uint32_t p0 = (sr_fp4_byte0(y[1], r0.w[1], divisor) << 4) | sr_fp4_byte0(y[0], r0.w[0], divisor);
+    const uint32_t p1 = (sr_fp4_byte0(y[3], r0.w[3], divisor) << 4) | sr_fp4_byte0(y[2], r0.w[2], divisor);
+    const uint32_t p2 = (sr_fp4_byte0(y[5], r1.w[1], divisor) << 4) | sr_fp4_byte0(y[4], r1.w[0], divisor);
+    const uint32_t p3 = (sr_fp4_byte0(y[7], r1.w[3], divisor) << 4) | sr_fp4_byte0(y[6], r1.w[2], divisor);
+    // v_perm_b32(hi, lo, sel): selector byte 0-3 picks that byte of lo, 4-7 of hi, 0x0c gives 0
+    const uint32_t q01 = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);  // [p0.b0, p1.b0, 0, 0]
+    const uint32_t q23 = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);  // [0, 0, p2.b0, p3.b0]
+    return q01 | q23;
 }
 
 // ---------------------------------------------------------------------------- cross-lane ------

@@ -170,13 +170,13 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
         uint32_t sc = e8m0_from_amax_bits(amax);
         if (noclip) sc = e8m0_noclip(amax, sc);
         uint32_t w0, w1;
+        prescale_if_zero_scale<16>(v[u], sc);
+        const float div = e8m0_divisor(sc);
         if constexpr (SR) {
             const uint64_t index0 = (uint64_t)row[u] * (uint64_t)L + (uint64_t)grp[u] * 16u;
-            w0 = encode8_stochastic(v[u], sc, index0, key0, key1, stream_id);
-            w1 = encode8_stochastic(v[u] + 8, sc, index0 + 8u, key0, key1, stream_id);
+            w0 = encode8_stochastic(v[u], div, index0, key0, key1, stream_id);
+            w1 = encode8_stochastic(v[u] + 8, div, index0 + 8u, key0, key1, stream_id);
         } else {
-            prescale_if_zero_scale<16>(v[u], sc);
-            const float div = e8m0_divisor(sc);
             w0 = encode8_nearest(v[u], div);
             w1 = encode8_nearest(v[u] + 8, div);
         }
@@ -287,14 +287,14 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
                 uint32_t sc = e8m0_from_amax_bits(amax);
                 if (noclip) sc = e8m0_noclip(amax, sc);
                 uint32_t words[4];
+                prescale_if_zero_scale<32>(v[cc], sc);
+                const float div = e8m0_divisor(sc);
                 if constexpr (SR) {
                     const uint64_t index0 = (uint64_t)(c0 + tc) * (uint64_t)rows + (uint64_t)(r0 + 32 * blk);
 #pragma unroll
                     for (int wd = 0; wd < 4; ++wd)
-                        words[wd] = encode8_stochastic(v[cc] + 8 * wd, sc, index0 + 8 * wd, key0, key1, stream_id);
+                        words[wd] = encode8_stochastic(v[cc] + 8 * wd, div, index0 + 8 * wd, key0, key1, stream_id);
                 } else {
-                    prescale_if_zero_scale<32>(v[cc], sc);
-                    const float div = e8m0_divisor(sc);
 #pragma unroll
                     for (int wd = 0; wd < 4; ++wd) words[wd] = encode8_nearest(v[cc] + 8 * wd, div);
                 }
@@ -449,13 +449,13 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
             if (o1.noclip) sc = e8m0_noclip(amax, sc);
             const uint32_t o = r0 + tr, g = g1;   // quantized row, global 16-element group
             uint32_t w0, w1;
+            prescale_if_zero_scale<16>(v, sc);
+            const float div = e8m0_divisor(sc);
             if (o1.sr) {
                 const uint64_t index0 = (uint64_t)o * cols + 16u * g;
-                w0 = encode8_stochastic(v, sc, index0, o1.key0, o1.key1, o1.stream_id);
-                w1 = encode8_stochastic(v + 8, sc, index0 + 8u, o1.key0, o1.key1, o1.stream_id);
+                w0 = encode8_stochastic(v, div, index0, o1.key0, o1.key1, o1.stream_id);
+                w1 = encode8_stochastic(v + 8, div, index0 + 8u, o1.key0, o1.key1, o1.stream_id);
             } else {
-                prescale_if_zero_scale<16>(v, sc);
-                const float div = e8m0_divisor(sc);
                 w0 = encode8_nearest(v, div);
                 w1 = encode8_nearest(v + 8, div);
             }
@@ -505,14 +505,14 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
             uint32_t sc = e8m0_from_amax_bits(amax);
             if (o0.noclip) sc = e8m0_noclip(amax, sc);
             uint32_t words[4];
+            prescale_if_zero_scale<32>(v[cc], sc);
+            const float div = e8m0_divisor(sc);
             if (o0.sr) {
                 const uint64_t index0 = (uint64_t)(c0 + tc) * rows + r0 + 32 * blk;
 #pragma unroll
                 for (int wd = 0; wd < 4; ++wd)
-                    words[wd] = encode8_stochastic(v[cc] + 8 * wd, sc, index0 + 8 * wd, o0.key0, o0.key1, o0.stream_id);
+                    words[wd] = encode8_stochastic(v[cc] + 8 * wd, div, index0 + 8 * wd, o0.key0, o0.key1, o0.stream_id);
             } else {
-                prescale_if_zero_scale<32>(v[cc], sc);
-                const float div = e8m0_divisor(sc);
 #pragma unroll
                 for (int wd = 0; wd < 4; ++wd) words[wd] = encode8_nearest(v[cc] + 8 * wd, div);
             }
