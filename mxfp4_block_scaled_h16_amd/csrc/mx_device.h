@@ -122,28 +122,40 @@ struct Philox4 {
     uint32_t w[4];
 };
 
+// One round; TT is the truth table of the three-input XORs (0x96), or of their complement (0x69).
+template <int TT>
+__device__ __forceinline__ void philox_round(uint32_t &c0, uint32_t &c1, uint32_t &c2, uint32_t &c3,
+                                             uint32_t k0, uint32_t k1)
+{
+    const uint64_t p = (uint64_t)0xD2511F53u * c0;
+    const uint64_t q = (uint64_t)0xCD9E8D57u * c2;
+    // three-input XORs in one gfx950 bitop3 instruction each
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(q >> 32), c1, k0, TT);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p >> 32), c3, k1, TT);
+    c1 = (uint32_t)q;
+    c3 = (uint32_t)p;
+    c0 = n0;
+    c2 = n2;
+}
+
+// COMPLEMENT returns the bitwise complement of the four words; words 0 and 2 get it for free
+// from the last round's three-input XORs.
+template <bool COMPLEMENT = false>
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                  uint32_t k0, uint32_t k1)
 {
 #pragma unroll
-    for (int round = 0; round < 10; ++round) {
-        const uint64_t p = (uint64_t)0xD2511F53u * c0;
-        const uint64_t q = (uint64_t)0xCD9E8D57u * c2;
-        // three-input XORs (truth table 0x96) in one gfx950 bitop3 instruction each
-        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(q >> 32), c1, k0, 0x96);
-        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p >> 32), c3, k1, 0x96);
-        c1 = (uint32_t)q;
-        c3 = (uint32_t)p;
-        c0 = n0;
-        c2 = n2;
+    for (int round = 0; round < 9; ++round) {
+        philox_round<0x96>(c0, c1, c2, c3, k0, k1);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
+    philox_round<COMPLEMENT ? 0x69 : 0x96>(c0, c1, c2, c3, k0, k1);
     Philox4 r;
     r.w[0] = c0;
-    r.w[1] = c1;
+    r.w[1] = COMPLEMENT ? ~c1 : c1;
     r.w[2] = c2;
-    r.w[3] = c3;
+    r.w[3] = COMPLEMENT ? ~c3 : c3;
     return r;
 }
 
@@ -186,20 +198,21 @@ __device__ __forceinline__ void apply_signs(float *v, uint32_t bits)
 // defined (the compiler does not carry the other bytes of the destination through), so pairs
 // are merged with a shift and the four valid bytes gathered with byte permutes.
 
-// the code of y in bits 0-3 and 0 in bits 4-7; bits 8-31 undefined
-__device__ __forceinline__ uint32_t sr_fp4_byte0(float y, uint32_t r, float divisor)
+// the code of y in bits 0-3 and 0 in bits 4-7 (bits 8-31 undefined), given nr = ~r
+__device__ __forceinline__ uint32_t sr_fp4_byte0(float y, uint32_t nr, float divisor)
 {
     const f32x2 pair = {y, 0.0f};
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, ~r, divisor, 0);
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, nr, divisor, 0);
 }
 
 __device__ __forceinline__ uint32_t encode8_stochastic(const float *y, float divisor, uint64_t index0,
                                                        uint32_t key0, uint32_t key1, uint32_t stream_id)
 {
     const uint64_t c = index0 >> 2;
-    const Philox4 r0 = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), stream_id, 0u, key0, key1);
+    // complemented words (~r), as the conversion takes them
+    const Philox4 r0 = philox4x32_10<true>((uint32_t)c, (uint32_t)(c >> 32), stream_id, 0u, key0, key1);
     const uint64_t c1 = c + 1;
-    const Philox4 r1 = philox4x32_10((uint32_t)c1, (uint32_t)(c1 >> 32), stream_id, 0u, key0, key1);
+    const Philox4 r1 = philox4x32_10<true>((uint32_t)c1, (uint32_t)(c1 >> 32), stream_id, 0u, key0, key1);
     // byte 0 of p_k = codes of elements 2k (low nibble) and 2k + 1 (high nibble)
     const uint32_t p0 = (sr_fp4_byte0(y[1], r0.w[1], divisor) << 4) | sr_fp4_byte0(y[0], r0.w[0], divisor);
     const uint32_t p1 = (sr_fp4_byte0(y[3], r0.w[3], divisor) << 4) | sr_fp4_byte0(y[2], r0.w[2], divisor);
