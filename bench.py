@@ -307,41 +307,42 @@ def quantization_error(plan, rows=8):
     return out
 
 
+GEMM_ROWS = 512  # output rows of the oracle GEMM the CPU baseline times (10-15 s on 16 cores)
+
+
 def cpu_baseline(plan, h):
     """The oracle, untuned, on a bounded sample of the same step, projected to the whole step."""
     import numpy as np
     import oracle
+    t_begin = time.perf_counter()
     threads = oracle.num_threads()
     acts, per_proj = plan.host["acts"], plan.host["proj"]
-    # quantization rate: one sample per launch kind, about a second each
+    # quantization rate: one whole operand per launch kind (rows of an activation, the transposed
+    # SR quantization of dY, the transposed RNE quantization of W)
     any_act = next(iter(acts.values()))
     name0 = plan.projs[0][0]
     w0, dy0 = per_proj[name0]
-    rows = min(any_act.shape[0], 256)
+    rows = any_act.shape[0]
     t0 = time.perf_counter()
-    oracle.quantize(np.ascontiguousarray(any_act[:rows]), 1, h, oracle.RNE)
-    rate_rows = rows * any_act.shape[1] / (time.perf_counter() - t0)
-    ncol = min(dy0.shape[1], 128)
-    sl = np.ascontiguousarray(dy0[:, :ncol])
+    oracle.quantize(np.ascontiguousarray(any_act), 1, h, oracle.RNE)
+    rate_rows = any_act.size / (time.perf_counter() - t0)
     t0 = time.perf_counter()
-    oracle.quantize(sl, 0, h, oracle.SR, seed=0x5EED)
-    rate_cols_sr = sl.size / (time.perf_counter() - t0)
-    ncolw = min(w0.shape[1], 128)
-    slw = np.ascontiguousarray(w0[:, :ncolw])
+    oracle.quantize(dy0, 0, h, oracle.SR, seed=0x5EED)
+    rate_cols_sr = dy0.size / (time.perf_counter() - t0)
     t0 = time.perf_counter()
-    oracle.quantize(slw, 0, h, oracle.RNE)
-    rate_cols = slw.size / (time.perf_counter() - t0)
+    oracle.quantize(w0, 0, h, oracle.RNE)
+    rate_cols = w0.size / (time.perf_counter() - t0)
     t_quant = 0.0
     for label, kind, spec, work in plan.op_list:
         for q in (spec if kind == "dual" else (spec,) if kind == "quant" else ()):
             axis, rnd = q[3], q[4]
             rate = rate_rows if axis == 1 else (rate_cols_sr if rnd == "sr" else rate_cols)
             t_quant += work / rate
-    # GEMM rate: 8 output rows of the first projection's Fprop-shaped product
-    qa = oracle.quantize(np.ascontiguousarray(any_act[:8]), 1, h, oracle.RNE)
+    # GEMM rate: the first GEMM_ROWS output rows of the first projection's Fprop-shaped product
+    qa = oracle.quantize(np.ascontiguousarray(any_act[:GEMM_ROWS]), 1, h, oracle.RNE)
     qb = oracle.quantize(w0, 1, h, oracle.RNE, stream=1) if w0.shape[1] == any_act.shape[1] else None
     if qb is None:
-        qa = oracle.quantize(np.ascontiguousarray(dy0[:8]), 1, h, oracle.RNE)
+        qa = oracle.quantize(np.ascontiguousarray(dy0[:GEMM_ROWS]), 1, h, oracle.RNE)
         qb = oracle.quantize(w0, 0, h, oracle.RNE, stream=1)
     t0 = time.perf_counter()
     c = oracle.gemm(*qa, *qb, alpha=oracle.alpha_for(h))
@@ -350,9 +351,11 @@ def cpu_baseline(plan, h):
     step_flops = sum(work for label, kind, spec, work in plan.op_list if kind == "gemm")
     t_step = t_quant + step_flops / rate_gemm
     return {"value": step_flops / t_step / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": ("quantize %d rows (RNE, along rows), %d columns of dY (transposed, SR), %d columns of W "
-                       "(transposed, RNE); GEMM 8 output rows of %s; projected to the whole step"
-                       % (rows, ncol, ncolw, name0)),
+            "sample": ("quantize all %d rows of an activation (RNE, along rows), all of dY %s (transposed, SR) "
+                       "and all of W %s (transposed, RNE); GEMM %d output rows of %s; projected to the whole "
+                       "step" % (rows, "x".join(map(str, dy0.shape)), "x".join(map(str, w0.shape)),
+                                 c.shape[0], name0)),
+            "cpu_seconds": round(time.perf_counter() - t_begin, 2),
             "gemm_gflops": rate_gemm / 1e9, "quantize_melem_s": rate_rows / 1e6,
             "step_seconds_projected": t_step}
 
