@@ -307,7 +307,7 @@ def quantization_error(plan, rows=8):
     return out
 
 
-GEMM_ROWS = 512  # output rows of the oracle GEMM the CPU baseline times (10-15 s on 16 cores)
+GEMM_ROWS = 1024  # output rows of the oracle GEMM the CPU baseline times (about 15 s on 16 cores)
 
 
 def cpu_baseline(plan, h):
