@@ -422,7 +422,8 @@ def run_timed(plan, steps, warmup):
     """W untimed warm-up steps, then EXACTLY K timed steps bracketed by device synchronizations
     (host clock, no per-launch instrumentation), then K more steps with fence-free HIP events
     around every launch on the launch stream for the per-kernel durations.
-    Returns (ms per step of the timed steps, average ms of each launch of the step)."""
+    Returns (ms per step of the timed steps, average ms of each launch of the step, ms of each
+    instrumented step from its first launch's start to its last launch's end)."""
     import numpy as np
     import torch
     for s in range(warmup):
@@ -449,8 +450,9 @@ def run_timed(plan, steps, warmup):
     torch.cuda.synchronize()
     per_launch = np.array([[ev.elapsed_ms(marks[s][i], marks[s][i + 1]) for i in range(n_launch)]
                            for s in range(steps)])
+    per_step = np.array([ev.elapsed_ms(marks[s][0], marks[s][n_launch]) for s in range(steps)])
     ev.close()
-    return (t1 - t0) * 1e3 / steps, per_launch.mean(0)
+    return (t1 - t0) * 1e3 / steps, per_launch.mean(0), per_step
 
 
 def machine_ceilings(settle_s=0.25, reps=10):
@@ -612,7 +614,7 @@ def main():
     torch.cuda.synchronize()
 
     settle_steps = settle(plan, args.settle)
-    ms_per_step, avg_ms = run_timed(plan, args.steps, args.warmup)
+    ms_per_step, avg_ms, step_ms = run_timed(plan, args.steps, args.warmup)
     step_flops = sum(w for _, kind, _, w in plan.op_list if kind == "gemm")
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -648,7 +650,7 @@ def main():
     if args.workload == "qkv" and "F" in passes:
         fplan = Plan(mx, torch, "qkv_fprop", h, sets, dual=False, host=plan.host)
         settle(fplan, min(args.settle, 0.25))
-        f_ms, f_avg = run_timed(fplan, args.steps, args.warmup)
+        f_ms, f_avg, _ = run_timed(fplan, args.steps, args.warmup)
         f_flops = sum(w for _, kind, _, w in fplan.op_list if kind == "gemm")
         f_gemm_s = sum(float(t) * 1e-3 for (_, kind, _, _), t in zip(fplan.op_list, f_avg) if kind == "gemm")
         f_q_s = sum(float(t) * 1e-3 for (_, kind, _, _), t in zip(fplan.op_list, f_avg) if kind != "gemm")
@@ -696,7 +698,10 @@ def main():
                    "input_sets": sets},
         "timing": {"settle_s": args.settle, "settle_steps": settle_steps,
                    "value": "host clock over the K timed steps, no per-launch instrumentation",
-                   "kernels": "a second pass of K steps with fence-free HIP events around every launch"},
+                   "kernels": "a second pass of K steps with fence-free HIP events around every launch",
+                   "instrumented_step_ms": {"median": round(float(np.median(step_ms)), 4),
+                                            "min": round(float(step_ms.min()), 4),
+                                            "max": round(float(step_ms.max()), 4)}},
         "roofline": roofline, "quantizer": quantizer, "kernels": kernels, "cpu_baseline": cpu,
     }
     if fprop is not None:

@@ -21,6 +21,27 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// ---------------------------------------------------------------------------- magnitudes ------
+// |x| as an unsigned bit pattern orders like |x|, with NaN above +inf.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// largest |v[i]| of N values as a bit pattern
+template <int N>
+__device__ __forceinline__ uint32_t amax_bits(const float *v)
+{
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) m = max(m, abs_bits(v[i]));
+    return m;
+}
+
+// The largest |x * norm| from the largest |x| (bit pattern amax): binary32 multiplication by a
+// positive number is monotonic in |x|, so scaling the maximum gives the maximum of the scaled.
+__device__ __forceinline__ uint32_t scaled_amax(uint32_t amax, float norm)
+{
+    return abs_bits(__uint_as_float(amax) * norm);
+}
+
 // ---------------------------------------------------------------------------- block Hadamard --
 // Unnormalised Sylvester transform of n values held in registers, binary32, strides 1, 2, 4, ...,
 // pair update (u, w) -> (u + w, u - w). The upper element is always u - w (never -(w - u)) so
@@ -41,6 +62,38 @@ __device__ __forceinline__ void fwht_regs(float *v)
     }
 }
 
+// fwht_regs<N> that also returns the largest |output| as a binary32 bit pattern. In the last
+// stage the larger of |u + w| and |u - w| is |u| + |w|, and binary32 rounding is monotonic and
+// symmetric, so the larger of the two rounded outputs' magnitudes is the rounded |u| + |w|: one
+// add with absolute-value operands per output pair instead of two masks and a max. A NaN or
+// infinity among the outputs gives a pattern >= 0x7F800000 here as well (infinity minus infinity
+// becomes infinity instead of NaN), which is all the scale rule looks at.
+template <int N>
+__device__ __forceinline__ uint32_t fwht_regs_amax(float *v)
+{
+#pragma unroll
+    for (int s = 1; s < N / 2; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if ((i & s) == 0) {
+                const float u = v[i], w = v[i + s];
+                v[i] = u + w;
+                v[i + s] = u - w;
+            }
+        }
+    }
+    uint32_t m = 0u;
+    constexpr int s = N / 2;
+#pragma unroll
+    for (int i = 0; i < s; ++i) {
+        const float u = v[i], w = v[i + s];
+        v[i] = u + w;
+        v[i + s] = u - w;
+        m = max(m, __float_as_uint(fabsf(u) + fabsf(w)));
+    }
+    return m;
+}
+
 // Rotate 32 values that form one MX block: H in {0, 16, 32}.
 template <int H>
 __device__ __forceinline__ void rotate_block(float *v)
@@ -53,6 +106,22 @@ __device__ __forceinline__ void rotate_block(float *v)
     }
 }
 
+// Rotate the 32 values of one MX block (H in {0, 16, 32}, as rotate_block) and return their
+// largest magnitude as a bit pattern.
+template <int H>
+__device__ __forceinline__ uint32_t rotate_block_amax(float *v)
+{
+    if constexpr (H == 16) {
+        const uint32_t a = fwht_regs_amax<16>(v);
+        const uint32_t b = fwht_regs_amax<16>(v + 16);
+        return max(a, b);
+    } else if constexpr (H == 32) {
+        return fwht_regs_amax<32>(v);
+    } else {
+        return amax_bits<32>(v);
+    }
+}
+
 // v[i] *= s in binary32 (the orthonormal rotation's 1/sqrt(h), after the transform)
 template <int N>
 __device__ __forceinline__ void scale_values(float *v, float s)
@@ -62,9 +131,6 @@ __device__ __forceinline__ void scale_values(float *v, float s)
 }
 
 // ---------------------------------------------------------------------------- scale -----------
-// |x| as an unsigned bit pattern orders like |x|, with NaN above +inf.
-__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
-
 // E8M0 byte from the block's largest |value| bit pattern: biased exponent E of amax gives
 // floor(log2 amax) = E - 127, so the shared exponent E - 127 - 2 is the byte E - 2 (clamped at 0).
 __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits)

@@ -158,14 +158,21 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 #pragma unroll
     for (int u = 0; u < kRowsUnroll; ++u) {
         if constexpr (RHT) apply_signs<16>(v[u], (rht_sign_word(grp[u] / 2, key0, key1) >> (16 * (grp[u] % 2))) & 0xFFFFu);
-        if constexpr (H >= 16) {
-            fwht_regs<16>(v[u]);
-            if constexpr (H == 32) fwht_cross_stage<1, 16>(v[u], upper1);
-            if (norm != 1.0f) scale_values<16>(v[u], norm);
+        uint32_t amax;
+        if constexpr (H == 16) {
+            amax = fwht_regs_amax<16>(v[u]);
+            if (norm != 1.0f) {
+                scale_values<16>(v[u], norm);
+                amax = scaled_amax(amax, norm);
+            }
+        } else {
+            if constexpr (H == 32) {
+                fwht_regs<16>(v[u]);
+                fwht_cross_stage<1, 16>(v[u], upper1);
+                if (norm != 1.0f) scale_values<16>(v[u], norm);
+            }
+            amax = amax_bits<16>(v[u]);
         }
-        uint32_t amax = 0u;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = max(amax, abs_bits(v[u][i]));
         amax = max(amax, quad_xor<1>(amax));
         uint32_t sc = e8m0_from_amax_bits(amax);
         if (noclip) sc = e8m0_noclip(amax, sc);
@@ -279,11 +286,11 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
             for (int cc = 0; cc < kColsPerThread; ++cc) {
                 const uint32_t tc = cp * kColsPerThread + cc;  // tile column = quantized row
                 if constexpr (RHT) apply_signs<32>(v[cc], signs);
-                rotate_block<H>(v[cc]);
-                if (H > 0 && norm != 1.0f) scale_values<32>(v[cc], norm);
-                uint32_t amax = 0u;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[cc][i]));
+                uint32_t amax = rotate_block_amax<H>(v[cc]);
+                if (H > 0 && norm != 1.0f) {
+                    scale_values<32>(v[cc], norm);
+                    amax = scaled_amax(amax, norm);
+                }
                 uint32_t sc = e8m0_from_amax_bits(amax);
                 if (noclip) sc = e8m0_noclip(amax, sc);
                 uint32_t words[4];
@@ -436,14 +443,21 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
                 }
             }
             if constexpr (RHT) apply_signs<16>(v, row_signs);
-            if constexpr (H >= 16) {
-                fwht_regs<16>(v);
-                if constexpr (H == 32) fwht_cross_stage<1, 16>(v, upper1);
-                if (norm != 1.0f) scale_values<16>(v, norm);
+            uint32_t amax;
+            if constexpr (H == 16) {
+                amax = fwht_regs_amax<16>(v);
+                if (norm != 1.0f) {
+                    scale_values<16>(v, norm);
+                    amax = scaled_amax(amax, norm);
+                }
+            } else {
+                if constexpr (H == 32) {
+                    fwht_regs<16>(v);
+                    fwht_cross_stage<1, 16>(v, upper1);
+                    if (norm != 1.0f) scale_values<16>(v, norm);
+                }
+                amax = amax_bits<16>(v);
             }
-            uint32_t amax = 0u;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) amax = max(amax, abs_bits(v[i]));
             amax = max(amax, quad_xor<1>(amax));
             uint32_t sc = e8m0_from_amax_bits(amax);
             if (o1.noclip) sc = e8m0_noclip(amax, sc);
@@ -497,11 +511,11 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
         for (int cc = 0; cc < 2; ++cc) {
             const uint32_t tc = F32 ? lane + 64 * cc : 2 * lane + cc;  // tile column = quantized row
             if constexpr (RHT) apply_signs<32>(v[cc], col_signs);
-            rotate_block<H>(v[cc]);
-            if (H > 0 && norm != 1.0f) scale_values<32>(v[cc], norm);
-            uint32_t amax = 0u;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) amax = max(amax, abs_bits(v[cc][i]));
+            uint32_t amax = rotate_block_amax<H>(v[cc]);
+            if (H > 0 && norm != 1.0f) {
+                scale_values<32>(v[cc], norm);
+                amax = scaled_amax(amax, norm);
+            }
             uint32_t sc = e8m0_from_amax_bits(amax);
             if (o0.noclip) sc = e8m0_noclip(amax, sc);
             uint32_t words[4];
