@@ -68,7 +68,8 @@ def test_float32_input_heavy_tails(axis):
 
 @pytest.mark.parametrize("axis", [1, 0])
 def test_special_values(axis):
-    """Zeros, signed zeros, subnormals, NaN, infinities, overflow after rotation and exact ties."""
+    """Zeros, signed zeros, subnormals, NaN, infinities (also +inf and -inf in one butterfly),
+    overflow after rotation and exact ties."""
     rng = np.random.default_rng(8)
     x = np.zeros((64, 128), dtype=np.float32)
     x[0, :] = 0.0
@@ -81,6 +82,12 @@ def test_special_values(axis):
                                 -2.5, -3.5, -5, 7], dtype=np.float32), 8)
     x[7, :] = -np.abs(rng.standard_normal(128)).astype(np.float32) * 1e-3
     x[8:, :] = rng.standard_normal((56, 128)).astype(np.float32)
+    # +inf and -inf meeting in the last butterfly stage (stride 8 of H16, stride 16 of H32), and
+    # a pair whose difference overflows there
+    x[8, 0], x[8, 8] = np.inf, -np.inf
+    x[9, 32], x[9, 48] = np.inf, -np.inf
+    x[10, 64], x[10, 72] = 3.0e38, -3.0e38
+    x[11, 96], x[11, 112] = 3.0e38, -3.0e38
     xin = x if axis == 1 else np.ascontiguousarray(x.T)
     for h in (0, 16, 32):
         for rnd in (0, 1):

@@ -84,6 +84,13 @@ def test_dual_special_values():
                     dtype=np.float32)
     x[10, :] = np.tile(ties, 8)
     x[:, 11] = np.tile(ties, 8)
+    # +inf and -inf meeting in the last butterfly stage, along a row and along a column, and a
+    # pair whose difference overflows there
+    x[12, 32], x[12, 40] = np.inf, -np.inf
+    x[16, 13], x[24, 13] = np.inf, -np.inf
+    x[32, 15], x[48, 15] = np.inf, -np.inf
+    x[13, 64], x[13, 80] = 3.0e38, -3.0e38
+    x[96, 17], x[104, 17] = 3.0e38, -3.0e38
     for h in (0, 16, 32):
         for rnd1, rnd0 in ((0, 0), (1, 1)):
             check_dual(x, h, rnd1, rnd0, seed1=5, seed0=6, what="special f32")
