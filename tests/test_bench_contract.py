@@ -24,3 +24,25 @@ def test_workloads_name_their_shapes():
     assert bench.WORKLOADS["layer"][1] == bench.LLAMA_PROJ and len(bench.LLAMA_PROJ) == 7
     assert bench.DUAL_BYTES_PER_ELEM == 2 + 2 * (0.5 + 1 / 32)
     assert bench.QUANT_BYTES_PER_ELEM == 2 + 0.5 + 1 / 32
+
+
+def test_cpu_baseline_leg_on_a_small_plan():
+    """The benchmark's oracle leg on a stub plan with small tensors: it times whole-operand
+    quantizations and the oracle GEMM and reports a positive rate with its thread count."""
+    import types
+
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    from synth import inputs
+    M, K, N = 256, 512, 256
+    x, w, dy = inputs.linear_inputs(M, K, N, seed=0)
+    plan = types.SimpleNamespace(
+        host={"acts": {"x": x}, "proj": {"small": (w, dy)}}, projs=[("small", K, N)],
+        op_list=[("quant x", "quant", (None, "act", "x", 1, "rne", 0, 0, None, None), M * K),
+                 ("quant dY", "quant", (None, "dy", "small", 0, "sr", 0, 0, None, None), M * N),
+                 ("gemm", "gemm", None, 2.0 * M * N * K)])
+    r = bench.cpu_baseline(plan, 16)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
+    assert r["value"] > 0 and r["gemm_gflops"] > 0 and r["cpu_seconds"] >= 0
+    assert "output rows" in r["sample"] and np.isfinite(r["step_seconds_projected"])
