@@ -214,17 +214,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
-constexpr int kBM = 256, kBN = 256;
+constexpr int kBM = 256, kBN = 256;                  // the main workgroup tile
 constexpr int kStageK = 128;                          // K values per stage
 constexpr int kRowBytes = kStageK / 2;                // 64 bytes of codes per row per stage
-constexpr int kABytes = kBM * kRowBytes;              // 16 KB
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;  // 32 KB
 constexpr int kNumBuf = 4;                            // stage ring; a group = 4 stages
-constexpr int kScaleSlot = (kBM + kBN) * 16;          // 8 KB: 16 scale bytes per row per group
-constexpr int kScaleBase = kNumBuf * kStageBytes;     // two scale slots after the stage ring
-constexpr int kLdsBytes = kScaleBase + 2 * kScaleSlot;  // 144 KB
 constexpr int kRowsPerDma = 1024 / kRowBytes;         // one wave-wide 16 B/lane DMA covers 16 rows
 constexpr int kGemmWaves = 8;                         // wavefronts per workgroup (4 or 8)
+constexpr int kComputeUnits = 256;                    // MI355X
 
 __device__ __forceinline__ int chunk_perm(int row) { return (row >> 2) & 3; }
 
@@ -246,29 +242,43 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Geometry of the pipelined kernel with NW wavefronts: a 2 x (NW / 2) arrangement of wave tiles
-// of 128 rows (four 32-row MFMA tiles of A) by 512 / NW columns (FJ 32-column tiles of B).
-template <int NW>
+// Geometry of the pipelined kernel with NW wavefronts and a T x T workgroup tile: a 2 x (NW / 2)
+// arrangement of wave tiles of T / 2 rows (FI 32-row MFMA tiles of A) by 2 T / NW columns (FJ
+// 32-column tiles of B). T = 256 is the main tile (one workgroup per CU); T = 128 with four
+// wavefronts serves products with fewer 256 x 256 tiles than CUs (half the LDS, two workgroups
+// per CU).
+template <int NW, int T = kBM>
 struct Geo {
-    static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts");
-    static constexpr int kWaveCols = 512 / NW;
-    static constexpr int FI = 4, FJ = kWaveCols / 32;
-    static constexpr int kDmaPerOperand = kBM / kRowsPerDma / NW;  // per wavefront and stage
+    static_assert(((NW == 4 || NW == 8) && T == 256) || (NW == 4 && T == 128), "pipelined geometries");
+    static constexpr int kTile = T;
+    static constexpr int kABytes = T * kRowBytes;                 // 16 KB for T = 256
+    static constexpr int kStageBytes = 2 * T * kRowBytes;         // 32 KB
+    static constexpr int kScaleSlot = 2 * T * 16;                 // 8 KB: 16 scale bytes per row per group
+    static constexpr int kScaleBase = kNumBuf * kStageBytes;      // two scale slots after the stage ring
+    static constexpr int kLdsBytes = kScaleBase + 2 * kScaleSlot; // 144 KB
+    static constexpr int kWaveRows = T / 2;
+    static constexpr int kWaveCols = 2 * T / NW;
+    static constexpr int FI = kWaveRows / 32, FJ = kWaveCols / 32;
+    static constexpr int kDmaPerOperand = T / kRowsPerDma / NW;   // per wavefront and stage
     static constexpr int kDmaPerStage = 2 * kDmaPerOperand;
-    static constexpr int kDmaPerScales = 8 / NW;                    // per wavefront and group
+    static constexpr int kScaleDmas = 2 * T / 64;                 // 64-row scale DMAs per group
+    static constexpr int kDmaPerScales = kScaleDmas / NW;         // per wavefront and group
+    static constexpr int kMinBlocks = T == 128 ? 2 : 1;           // workgroups per CU
 };
 
 // EPI: kEpiF32 writes FP32 c = alpha * A B^T (out.c a float pointer; no other epilogue code is
 // compiled in), kEpiF32Beta adds beta * c, kEpiBF16 writes bf16 (with beta * c).
-template <int NW, bool TILED, int EPI>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
+template <int NW, bool TILED, int EPI, int TILE = kBM>
+__global__ __launch_bounds__(64 * NW, (Geo<NW, TILE>::kMinBlocks)) void gemm_mxfp4_pipelined(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
     int M, int N, int K, OutSpec out, int tiles_m, int tiles_n, int splits, float *__restrict__ partials)
 {
-    using G = Geo<NW>;
+    using G = Geo<NW, TILE>;
     constexpr int FI = G::FI, FJ = G::FJ;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+    constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes, kScaleSlot = G::kScaleSlot;
+    constexpr int kScaleBase = G::kScaleBase;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::kLdsBytes];
 
     // tile order: consecutive workgroups are spread over the 8 XCDs; give each XCD a contiguous
     // range of tiles, walked column-panel by column-panel in groups of 8 row panels
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     const int gm = min(8, tiles_m - g0);
     const int tm = g0 + (t % group) % gm;
     const int tn = (t % group) / gm;
-    const int m0 = tm * kBM, n0 = tn * kBN;
+    const int m0 = tm * TILE, n0 = tn * TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -310,34 +320,42 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
             b_off[u] = (uint32_t)(min(n0 + row, N - 1) * ldb + 16 * chunk);
         }
     }
-    // scale DMA: 64 rows of one operand per instruction, 16 bytes (one group) per lane; with 4
-    // wavefronts each brings rows [64 w, + 64) of both operands, with 8 wavefront w < 4 brings
-    // A rows [64 w, + 64) and wavefront w >= 4 B rows [64 (w - 4), + 64)
+    // scale DMA: 64 rows of one operand per instruction, 16 bytes (one group) per lane. Main tile:
+    // with 4 wavefronts each brings rows [64 w, + 64) of both operands, with 8 wavefront w < 4
+    // brings A rows [64 w, + 64) and wavefront w >= 4 B rows [64 (w - 4), + 64). 128-row tile:
+    // wavefronts 0, 1 bring A rows [64 w, + 64), wavefronts 2, 3 B rows [64 (w - 2), + 64).
     uint32_t s_off[G::kDmaPerScales];
     int s_dst[G::kDmaPerScales];
     const uint8_t *s_src[G::kDmaPerScales];
 #pragma unroll
     for (int u = 0; u < G::kDmaPerScales; ++u) {
-        const bool is_b = NW == 4 ? u == 1 : wave >= 4;
-        const int row = 64 * (NW == 4 ? wave : (wave & 3)) + lane;
+        bool is_b;
+        int q64;
+        if constexpr (TILE == 256) {
+            is_b = NW == 4 ? u == 1 : wave >= 4;
+            q64 = NW == 4 ? wave : (wave & 3);
+        } else {
+            is_b = wave >= 2;
+            q64 = wave & 1;
+        }
+        const int row = 64 * q64 + lane;
         s_src[u] = is_b ? bs : as;
         if constexpr (TILED) {
             // 64-row x 512-K scale blocks of 1024 bytes, 16 per row
-            const int q64 = (NW == 4 ? wave : (wave & 3));
             s_off[u] = (uint32_t)(((is_b ? n0 : m0) / 64 + q64) * (K / 512) * 1024 + lane * 16);
         } else {
             s_off[u] = (uint32_t)(is_b ? min(n0 + row, N - 1) * ldbs : min(m0 + row, M - 1) * ldas);
         }
-        s_dst[u] = (is_b ? kBM * 16 : 0) + 1024 * (NW == 4 ? wave : (wave & 3));
+        s_dst[u] = (is_b ? TILE * 16 : 0) + 1024 * q64;
     }
     // fragment and scale reads of this lane
     const int perm = chunk_perm(r);
-    const int a_frag = (wm * 128 + r) * kRowBytes;
+    const int a_frag = (wm * G::kWaveRows + r) * kRowBytes;
     const int b_frag = kABytes + (wn * G::kWaveCols + r) * kRowBytes;
     const int chunk0 = 16 * ((0 + half) ^ perm);
     const int chunk1 = 16 * ((2 + half) ^ perm);
-    const int sa_lds = kScaleBase + 16 * (wm * 128 + r);
-    const int sb_lds = kScaleBase + 16 * (kBM + wn * G::kWaveCols + r);
+    const int sa_lds = kScaleBase + 16 * (wm * G::kWaveRows + r);
+    const int sb_lds = kScaleBase + 16 * (TILE + wn * G::kWaveCols + r);
 
     const int stage0 = split * (K / kStageK / splits);  // first stage of this split
     auto dma = [&](int buf, int stage) {
@@ -514,7 +532,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     const float alpha = out.alpha;
     // split-K partials are FP32 whatever the variant: a bf16 variant decides per launch
     const bool bf16_now = EPI == kEpiBF16 && out.bf16;
-    const bool full_cols = n0 + kBN <= N && (bf16_now ? out_vector_ok<true>(out) : out_vector_ok<false>(out));
+    const bool full_cols = n0 + TILE <= N && (bf16_now ? out_vector_ok<true>(out) : out_vector_ok<false>(out));
     if (full_cols) {
         // stage each 32-row slice of this wavefront's 128 x kWaveCols result through LDS so that
         // a store instruction writes whole rows (two rows of kWaveCols floats)
@@ -545,7 +563,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
                     const int rr = kRowsPerStore * p + lane / kLanesPerRow;
                     f32x4v v = *reinterpret_cast<const f32x4v *>(epi + rr * kEpiRow + cc * 4);
                     v = v * alpha;
-                    const int m = m0 + wm * 128 + 32 * i + rr;
+                    const int m = m0 + wm * G::kWaveRows + 32 * i + rr;
                     if (m < M) *reinterpret_cast<f32x4v *>(c + (int64_t)m * ldc + ncol) = v;
                 }
             } else {
@@ -554,7 +572,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
                     const int rr = kRowsPerStore * p + lane / kLanesPerRow;
                     f32x4v v = *reinterpret_cast<const f32x4v *>(epi + rr * kEpiRow + cc * 4);
                     v = v * alpha;
-                    const int m = m0 + wm * 128 + 32 * i + rr;
+                    const int m = m0 + wm * G::kWaveRows + 32 * i + rr;
                     if (m < M) {
                         if (bf16_now)
                             store4<true>(out, m, ncol, N, v, true);
@@ -568,7 +586,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_mxfp4_pipelined(
     }
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
-        const int m = m0 + wm * 128 + 32 * i + r;
+        const int m = m0 + wm * G::kWaveRows + 32 * i + r;
         if (m >= M) continue;
         float *crow = c + (int64_t)m * ldc;
 #pragma unroll
@@ -669,12 +687,34 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
                        (uintptr_t)workspace % 16 != 0))
         splits = 1;
     float *partials = splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    hipError_t e;
+    if (splits == 1 && tiles_m * tiles_n <= kComputeUnits / 2) {
+        // 256 x 256 tiles would leave at least half the compute units idle: 128 x 128 tiles, four
+        // wavefronts, two workgroups per CU, four times as many workgroups. Measured faster up to
+        // 128 large tiles (8192 x 1024 x 4096: 28.2 -> 24.6 us; 1024 x 4096 x 8192: 45.9 -> 24.0 us)
+        // and slower from 192 on (8192 x 1536 x 4096: 33.0 -> 35.2 us), where the small tiles'
+        // doubled operand traffic costs more than the extra workgroups gain.
+        constexpr int kSmall = 128;
+        const int sm = (int)((M + kSmall - 1) / kSmall), sn = (int)((N + kSmall - 1) / kSmall);
+        const auto run_small = [&](auto kernel) {
+            return launch(kernel, dim3((unsigned)(sm * sn)), dim3(64 * 4), 0, stream, aq, lda, as, ldas, bq, ldb, bs,
+                          ldbs, (int)M, (int)N, (int)K, out, sm, sn, 1, (float *)nullptr);
+        };
+        if (tiled)
+            e = epi == kEpiBF16 ? run_small(gemm_mxfp4_pipelined<4, true, kEpiBF16, kSmall>)
+              : epi == kEpiF32Beta ? run_small(gemm_mxfp4_pipelined<4, true, kEpiF32Beta, kSmall>)
+                                   : run_small(gemm_mxfp4_pipelined<4, true, kEpiF32, kSmall>);
+        else
+            e = epi == kEpiBF16 ? run_small(gemm_mxfp4_pipelined<4, false, kEpiBF16, kSmall>)
+              : epi == kEpiF32Beta ? run_small(gemm_mxfp4_pipelined<4, false, kEpiF32Beta, kSmall>)
+                                   : run_small(gemm_mxfp4_pipelined<4, false, kEpiF32, kSmall>);
+        return e;
+    }
     const dim3 grid((unsigned)(tiles_m * tiles_n * splits)), block(64 * kGemmWaves);
     const auto run = [&](auto kernel) {
         return launch(kernel, grid, block, 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs, (int)M, (int)N, (int)K,
                       out, tiles_m, tiles_n, splits, partials);
     };
-    hipError_t e;
     if (tiled)
         e = epi == kEpiBF16 ? run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiBF16>)
           : epi == kEpiF32Beta ? run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32Beta>)
