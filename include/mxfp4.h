@@ -52,7 +52,10 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 8
+/* Raised whenever an entry point, a struct or the bits an entry point produces change. 9: the
+ * stochastic-rounding decision compares 22 random bits with the fractional position truncated to
+ * 22 bits (codes for |v| < 1 differ from 8). */
+#define MXFP4_ABI_VERSION 9
 
 typedef enum {
     MXFP4_OK = 0,

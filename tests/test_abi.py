@@ -63,7 +63,7 @@ def test_ceiling_library_exports_its_declared_symbols():
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 8
+    assert L.mxfp4_abi_version() == 9
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
