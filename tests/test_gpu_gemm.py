@@ -260,7 +260,7 @@ def _bf16_to_f64(t_u16):
 
 
 @pytest.mark.parametrize("M,N,K,layout,ws", [
-    (512, 768, 1024, "tiled", False),    # pipelined, whole tiles (LDS-staged epilogue)
+    (512, 768, 1024, "tiled", False),    # pipelined, 128 x 128 tiles, whole (LDS-staged epilogue)
     (300, 520, 1024, "tiled", False),    # ragged edges (direct epilogue)
     (512, 4096, 8192, "tiled", True),    # split-K partials + reduce kernel
     (200, 72, 96, "rows", False),        # K % 512 != 0: the plain kernel
@@ -319,4 +319,50 @@ def test_gemm_ex_epilogue(M, N, K, layout, ws, out_dtype, beta):
     bound = TOL * basis + (2.0 ** -8 * (np.abs(ref) + TOL * basis) if out_dtype == "bf16" else 0.0) + 1e-30
     err = np.abs(got - ref)
     assert np.isfinite(got).all()
+    assert (err <= bound).all(), "worst err %.3e vs bound %.3e" % (err.max(), bound[np.argmax(err - bound)])
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("beta", [0.0, 1.0, -0.5])
+def test_gemm_ex_epilogue_large_tiles(out_dtype, beta):
+    """The epilogue variants of the 256 x 256 tiles (more than 128 of them, so the large tiles
+    run), with ragged last row and column tiles: whole tiles through the LDS-staged epilogue,
+    the last column of tiles through the direct one. 4096 sampled outputs plus every corner of
+    the ragged edges, against the oracle; the same bar as the small shapes."""
+    from tests.gpu_util import tile
+    import mxfp4_block_scaled_h16_amd as mx
+    import torch
+    M, N, K = 2300, 3900, 512                     # 9 x 16 = 144 tiles of 256 x 256
+    rng = np.random.default_rng(11 + int(4 * beta) + (3 if out_dtype == "bf16" else 0))
+    aq, as_ = random_operand(rng, M, K)
+    bq, bs = random_operand(rng, N, K)
+    da = [_dev_u8(t.reshape(-(-M // 256) * 256, -1)) for t in tile(aq, as_, M, K)]
+    db = [_dev_u8(t.reshape(-(-N // 256) * 256, -1)) for t in tile(bq, bs, N, K)]
+    c_in = (rng.standard_normal((M, N)) * 50).astype(np.float32)
+    if out_dtype == "bf16":
+        c_bits = inputs.bf16_bits(c_in)
+        out = torch.from_numpy(c_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        c_in64 = _bf16_to_f64(c_bits)
+    else:
+        out = torch.from_numpy(c_in).cuda()
+        c_in64 = c_in.astype(np.float64)
+    if beta == 0.0:
+        out.fill_(float("nan"))  # must not be read
+    announce("gemm_ex large tiles", M, N, K, out_dtype, "beta", beta)
+    mx.gemm(*da, *db, alpha=0.25, out=out, layout="tiled", m=M, n=N, beta=beta)
+    if out_dtype == "bf16":
+        got = _bf16_to_f64(host(out.view(torch.int16)).view(np.uint16))
+    else:
+        got = host(out).astype(np.float64)
+    assert np.isfinite(got).all()
+    edge_m = [0, 255, 256, 2047, 2048, M - 1]
+    edge_n = [0, 255, 3583, 3584, 3840, N - 1]
+    ms = np.concatenate([rng.integers(0, M, 4096), np.repeat(edge_m, len(edge_n))])
+    ns = np.concatenate([rng.integers(0, N, 4096), np.tile(edge_n, len(edge_m))])
+    ref, basis = oracle.gemm_sampled(aq, as_, bq, bs, ms, ns, alpha=0.25)
+    if beta != 0.0:
+        ref = ref + beta * c_in64[ms, ns]
+        basis = basis + abs(beta) * np.abs(c_in64[ms, ns])
+    bound = TOL * basis + (2.0 ** -8 * (np.abs(ref) + TOL * basis) if out_dtype == "bf16" else 0.0) + 1e-30
+    err = np.abs(got[ms, ns] - ref)
     assert (err <= bound).all(), "worst err %.3e vs bound %.3e" % (err.max(), bound[np.argmax(err - bound)])
