@@ -366,3 +366,24 @@ def test_gemm_ex_epilogue_large_tiles(out_dtype, beta):
     bound = TOL * basis + (2.0 ** -8 * (np.abs(ref) + TOL * basis) if out_dtype == "bf16" else 0.0) + 1e-30
     err = np.abs(got[ms, ns] - ref)
     assert (err <= bound).all(), "worst err %.3e vs bound %.3e" % (err.max(), bound[np.argmax(err - bound)])
+
+
+def test_gemm_rows_layout_large_tiles():
+    """Row-major operands on the 256 x 256 tiles (144 of them, ragged last row and column): 4096
+    sampled outputs plus the ragged corners against the oracle."""
+    import mxfp4_block_scaled_h16_amd as mx
+    import torch
+    M, N, K = 2300, 3900, 1024
+    rng = np.random.default_rng(12)
+    aq, as_ = random_operand(rng, M, K)
+    bq, bs = random_operand(rng, N, K)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    announce("gemm rows layout large tiles", M, N, K)
+    mx.gemm(_dev_u8(aq), _dev_u8(as_), _dev_u8(bq), _dev_u8(bs), alpha=0.5, out=out, layout="rows")
+    got = host(out).astype(np.float64)
+    edge_m = [0, 255, 256, 2047, 2048, M - 1]
+    edge_n = [0, 255, 3583, 3584, 3840, N - 1]
+    ms = np.concatenate([rng.integers(0, M, 4096), np.repeat(edge_m, len(edge_n))])
+    ns = np.concatenate([rng.integers(0, N, 4096), np.tile(edge_n, len(edge_m))])
+    ref, basis = oracle.gemm_sampled(aq, as_, bq, bs, ms, ns, alpha=0.5)
+    assert_gemm_close(got[ms, ns], ref, basis, TOL, "rows layout, large tiles")
