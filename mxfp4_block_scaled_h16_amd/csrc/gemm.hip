@@ -23,6 +23,36 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kFmtFp4 = 4;  // format selector of the f8f6f4 MFMA family for E2M1
 
+// ------------------------------------------------------------------ accumulation chains -----
+// A scaled FP4 MFMA adds its block products (one per 32 K values: an exact integer times a power
+// of two) to the FP32 accumulator one at a time, in K order, rounding to nearest even after each
+// (GPU tests pin this: 1 followed by two blocks of 0.375 units in the last place stays 1, while
+// the same blocks before the 1 round it up). So an output accumulated in a single chain over K
+// values has gone through up to K / 32 roundings, and a term that passes through D roundings
+// carries a relative error of at most D u / (1 - D u), u = 2^-24. Every output meets
+// |c - c_exact| <= 1e-5 * sum_k |a_k b_k| as long as no term goes through more than
+// kMaxDepth = 167 roundings, i.e. K <= 5344 in one chain; a worst case reaches the bound (a
+// chain stuck at 1 while every later block adds just under half a unit in the last place).
+// Longer contractions are cut into segments: each segment accumulates from zero, and the
+// segments are added in their K order, which puts a term through at most (segment blocks) +
+// (number of segments) roundings. Split-K partials obey the same count.
+constexpr int kMaxDepth = 167;
+
+// Length, in units of `per_unit` blocks, of the segments that a chain of `units` units is cut
+// into; 0 when the whole chain is within the bound. Segments are as long as the bound allows for
+// the fewest of them; past about 7000 blocks (K of about 220 thousand) no two-level split meets
+// it, and the shortest segments are returned.
+int chain_segment(int64_t units, int per_unit)
+{
+    if (units * per_unit + 1 <= kMaxDepth) return 0;
+    for (int64_t c = 2; c <= units; ++c) {
+        const int64_t per = (units + c - 1) / c;
+        const int64_t segs = (units + per - 1) / per;
+        if (per * per_unit + segs <= kMaxDepth) return (int)per;
+    }
+    return 1;
+}
+
 // ---------------------------------------------------------------------------- output ---------
 // The general epilogue: c = alpha * (A B^T) + beta * c, stored as FP32 or bf16 (the FP32 value
 // rounded to nearest even by the hardware conversion). c is read only when beta != 0 (it may be
@@ -111,10 +141,14 @@ constexpr int kEpiBF16 = 2;     // bf16 with beta
 // tiles of 32 x 32); one K step = 64 (two MX blocks per row).
 constexpr int kTileM = 128, kTileN = 128, kWaveM = 64, kWaveN = 64;
 
+// FOLD: the accumulation chain restarts from zero every fold_steps MFMA steps, the finished
+// segments summed in K order in a second set of registers (contractions longer than one chain
+// may be).
+template <bool FOLD>
 __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
-    int M, int N, int K, OutSpec out)
+    int M, int N, int K, OutSpec out, int fold_steps)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -134,15 +168,21 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
         psb[i] = bs + (int64_t)row_b * ldbs + half;
     }
 
-    v16f acc[2][2];
+    v16f acc[2][2], seg_sum[FOLD ? 2 : 1][FOLD ? 2 : 1];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    if constexpr (FOLD) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) seg_sum[i][j] = v16f{};
+    }
 
-    for (int k0 = 0; k0 < K; k0 += 64) {
+    for (int k0 = 0, step = 1; k0 < K; k0 += 64, ++step) {
         // the second half of the last step is past K when K is an odd multiple of 32
         const bool live = k0 + 32 * half < K;
         v8i fa[2], fb[2];
@@ -168,6 +208,25 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     fa[i], fb[j], acc[i][j], kFmtFp4, kFmtFp4, 0, sa[i], 0, sb[j]);
+        if constexpr (FOLD) {
+            // end of a segment of the accumulation chain (not after the last step)
+            if (step % fold_steps == 0 && k0 + 64 < K) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        seg_sum[i][j] = seg_sum[i][j] + acc[i][j];
+                        acc[i][j] = v16f{};
+                    }
+            }
+        }
+    }
+    if constexpr (FOLD) {
+        // the last segment joins the earlier ones
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = seg_sum[i][j] + acc[i][j];
     }
 
 #pragma unroll
@@ -220,6 +279,11 @@ constexpr int kRowBytes = kStageK / 2;                // 64 bytes of codes per r
 constexpr int kNumBuf = 4;                            // stage ring; a group = 4 stages
 constexpr int kRowsPerDma = 1024 / kRowBytes;         // one wave-wide 16 B/lane DMA covers 16 rows
 constexpr int kGemmWaves = 8;                         // wavefronts per workgroup (4 or 8)
+// the tile of products whose contraction needs a segmented accumulation chain: 256 x 128, eight
+// wavefronts of 64 x 64 (a 128 x 64 wave tile has no registers left for the second accumulator
+// set). Measured against four wavefronts of 128 x 64 (one per SIMD, 455 registers): the same
+// (gate Dgrad 8192 x 4096 x 14336: 271.7 vs 276.8 us); 128 x 128 tiles: 285 us.
+constexpr int kFoldWaves = 8, kFoldTM = 256, kFoldTN = 128;
 constexpr int kComputeUnits = 256;                    // MI355X
 
 __device__ __forceinline__ int chunk_perm(int row) { return (row >> 2) & 3; }
@@ -242,39 +306,50 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Geometry of the pipelined kernel with NW wavefronts and a T x T workgroup tile: a 2 x (NW / 2)
-// arrangement of wave tiles of T / 2 rows (FI 32-row MFMA tiles of A) by 2 T / NW columns (FJ
-// 32-column tiles of B). T = 256 is the main tile (one workgroup per CU); T = 128 with four
-// wavefronts serves products with fewer 256 x 256 tiles than CUs (half the LDS, two workgroups
-// per CU).
-template <int NW, int T = kBM>
+// Geometry of the pipelined kernel: NW wavefronts, a TM x TN workgroup tile (TM rows of A, TN
+// rows of B), the wavefronts arranged WM x (NW / WM) with wave tiles of TM / WM rows (FI 32-row
+// MFMA tiles of A) by TN WM / NW columns (FJ 32-column tiles of B). Instantiated as:
+//  * 256 x 256, eight wavefronts of 128 x 64: the main tile (one workgroup per CU);
+//  * 128 x 128, four wavefronts of 64 x 64: products with fewer 256 x 256 tiles than half the
+//    CUs (half the LDS, two workgroups per CU);
+//  * 256 x 128, eight wavefronts of 64 x 64: contractions that need a segmented accumulation
+//    chain, whose second set of accumulators does not fit the main tile's wavefronts.
+template <int NW, int TM, int TN, int WM>
 struct Geo {
-    static_assert(((NW == 4 || NW == 8) && T == 256) || (NW == 4 && T == 128), "pipelined geometries");
-    static constexpr int kTile = T;
-    static constexpr int kABytes = T * kRowBytes;                 // 16 KB for T = 256
-    static constexpr int kStageBytes = 2 * T * kRowBytes;         // 32 KB
-    static constexpr int kScaleSlot = 2 * T * 16;                 // 8 KB: 16 scale bytes per row per group
+    static_assert(TM % 64 == 0 && TN % 64 == 0 && NW % WM == 0, "pipelined geometries");
+    static constexpr int kTileM = TM, kTileN = TN;
+    static constexpr int kABytes = TM * kRowBytes;                // 16 KB for TM = 256
+    static constexpr int kStageBytes = (TM + TN) * kRowBytes;     // 32 KB for 256 x 256
+    static constexpr int kScaleSlot = (TM + TN) * 16;             // 16 scale bytes per row per group
     static constexpr int kScaleBase = kNumBuf * kStageBytes;      // two scale slots after the stage ring
-    static constexpr int kLdsBytes = kScaleBase + 2 * kScaleSlot; // 144 KB
-    static constexpr int kWaveRows = T / 2;
-    static constexpr int kWaveCols = 2 * T / NW;
+    static constexpr int kLdsBytes = kScaleBase + 2 * kScaleSlot; // 144 KB for 256 x 256
+    static constexpr int kWavesM = WM, kWavesN = NW / WM;
+    static constexpr int kWaveRows = TM / kWavesM;
+    static constexpr int kWaveCols = TN / kWavesN;
     static constexpr int FI = kWaveRows / 32, FJ = kWaveCols / 32;
-    static constexpr int kDmaPerOperand = T / kRowsPerDma / NW;   // per wavefront and stage
-    static constexpr int kDmaPerStage = 2 * kDmaPerOperand;
-    static constexpr int kScaleDmas = 2 * T / 64;                 // 64-row scale DMAs per group
-    static constexpr int kDmaPerScales = kScaleDmas / NW;         // per wavefront and group
-    static constexpr int kMinBlocks = T == 128 ? 2 : 1;           // workgroups per CU
+    static constexpr int kDmaA = TM / kRowsPerDma / NW;           // per wavefront and stage
+    static constexpr int kDmaB = TN / kRowsPerDma / NW;
+    static_assert(kDmaA * kRowsPerDma * NW == TM && kDmaB * kRowsPerDma * NW == TN, "whole DMAs per wavefront");
+    static constexpr int kDmaPerStage = kDmaA + kDmaB;
+    static constexpr int kScaleChunks = (TM + TN) / 64;           // 64-row scale DMAs per group
+    static constexpr int kDmaPerScales = (kScaleChunks + NW - 1) / NW;  // per wavefront and group
+    static constexpr int kMinBlocks = kLdsBytes <= 80 * 1024 ? 2 : 1;   // workgroups per CU
 };
 
 // EPI: kEpiF32 writes FP32 c = alpha * A B^T (out.c a float pointer; no other epilogue code is
 // compiled in), kEpiF32Beta adds beta * c, kEpiBF16 writes bf16 (with beta * c).
-template <int NW, bool TILED, int EPI, int TILE = kBM>
-__global__ __launch_bounds__(64 * NW, (Geo<NW, TILE>::kMinBlocks)) void gemm_mxfp4_pipelined(
+// FOLD: the accumulation chain restarts from zero every fold_groups groups of four stages, the
+// finished segments summed in K order in a second set of registers (contractions longer than
+// one chain may be; only geometries with 64 x 64 wave tiles have the registers for it).
+template <int NW, bool TILED, int EPI, int TM = kBM, int TN = kBN, int WM = 2, bool FOLD = false>
+__global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void gemm_mxfp4_pipelined(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
-    int M, int N, int K, OutSpec out, int tiles_m, int tiles_n, int splits, float *__restrict__ partials)
+    int M, int N, int K, OutSpec out, int tiles_m, int tiles_n, int splits, float *__restrict__ partials,
+    int fold_groups)
 {
-    using G = Geo<NW, TILE>;
+    using G = Geo<NW, TM, TN, WM>;
+    static_assert(!FOLD || G::FI * G::FJ <= 4, "segmented accumulation needs wave tiles of at most 64 x 64");
     constexpr int FI = G::FI, FJ = G::FJ;
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes, kScaleSlot = G::kScaleSlot;
     constexpr int kScaleBase = G::kScaleBase;
@@ -292,61 +367,67 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TILE>::kMinBlocks)) void gemm_mxf
     const int gm = min(8, tiles_m - g0);
     const int tm = g0 + (t % group) % gm;
     const int tn = (t % group) / gm;
-    const int m0 = tm * TILE, n0 = tn * TILE;
+    const int m0 = tm * TM, n0 = tn * TN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % G::kWavesM, wn = wave / G::kWavesM;
     const int r = lane & 31, half = lane >> 5;
 
-    // code DMA: instruction u of this wavefront fills stage rows [16 (kDmaPerOperand wave + u),
-    // + 16) of each operand; lane L writes the 16 bytes at row + L / 4, physical chunk L % 4.
-    // Row-major operands: lane L reads its row's logical chunk (L % 4) ^ perm(row). Tiled operands
-    // already hold each 16-row x 128-K block as those 1024 bytes, in that order.
-    const int dma_row0 = kRowsPerDma * G::kDmaPerOperand * wave;
-    const int kblocks = K / kStageK;
-    uint32_t a_off[G::kDmaPerOperand], b_off[G::kDmaPerOperand];
+    // code DMA: instruction u of this wavefront fills stage rows [16 (kDmaA wave + u), + 16) of A
+    // (and likewise with kDmaB of B); lane L writes the 16 bytes at row + L / 4, physical chunk
+    // L % 4. Row-major operands: lane L reads its row's logical chunk (L % 4) ^ perm(row). Tiled
+    // operands already hold each 16-row x 128-K block as those 1024 bytes, in that order.
+    const int a_row0 = kRowsPerDma * G::kDmaA * wave;
+    const int b_row0 = kRowsPerDma * G::kDmaB * wave;
+    const uint32_t kblocks = (uint32_t)(K / kStageK);
+    uint32_t a_off[G::kDmaA], b_off[G::kDmaB];
 #pragma unroll
-    for (int u = 0; u < G::kDmaPerOperand; ++u) {
+    for (int u = 0; u < G::kDmaA; ++u) {
         if constexpr (TILED) {
-            const int rb = (dma_row0 + kRowsPerDma * u) / 16;
-            a_off[u] = (uint32_t)((m0 / 16 + rb) * kblocks * 1024 + lane * 16);
-            b_off[u] = (uint32_t)((n0 / 16 + rb) * kblocks * 1024 + lane * 16);
+            const uint32_t rb = (uint32_t)(m0 + a_row0 + kRowsPerDma * u) / 16;
+            a_off[u] = rb * kblocks * 1024u + (uint32_t)lane * 16u;
         } else {
-            const int row = dma_row0 + kRowsPerDma * u + lane / 4;
+            const int row = a_row0 + kRowsPerDma * u + lane / 4;
             const int chunk = (lane % 4) ^ chunk_perm(row);
             a_off[u] = (uint32_t)(min(m0 + row, M - 1) * lda + 16 * chunk);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < G::kDmaB; ++u) {
+        if constexpr (TILED) {
+            const uint32_t rb = (uint32_t)(n0 + b_row0 + kRowsPerDma * u) / 16;
+            b_off[u] = rb * kblocks * 1024u + (uint32_t)lane * 16u;
+        } else {
+            const int row = b_row0 + kRowsPerDma * u + lane / 4;
+            const int chunk = (lane % 4) ^ chunk_perm(row);
             b_off[u] = (uint32_t)(min(n0 + row, N - 1) * ldb + 16 * chunk);
         }
     }
-    // scale DMA: 64 rows of one operand per instruction, 16 bytes (one group) per lane. Main tile:
-    // with 4 wavefronts each brings rows [64 w, + 64) of both operands, with 8 wavefront w < 4
-    // brings A rows [64 w, + 64) and wavefront w >= 4 B rows [64 (w - 4), + 64). 128-row tile:
-    // wavefronts 0, 1 bring A rows [64 w, + 64), wavefronts 2, 3 B rows [64 (w - 2), + 64).
+    // scale DMA: 64 rows of one operand per instruction, 16 bytes (one group) per lane. The
+    // tile's 64-row chunks (A's first, then B's) go round-robin over the wavefronts: instruction u
+    // of wavefront w brings chunk (w + NW u) mod kScaleChunks. Where the chunks do not divide
+    // evenly, the last wavefronts load a chunk a second time (the same bytes to the same place),
+    // so that every wavefront issues the same number of loads and its vmcnt waits count alike.
     uint32_t s_off[G::kDmaPerScales];
     int s_dst[G::kDmaPerScales];
     const uint8_t *s_src[G::kDmaPerScales];
 #pragma unroll
     for (int u = 0; u < G::kDmaPerScales; ++u) {
-        bool is_b;
-        int q64;
-        if constexpr (TILE == 256) {
-            is_b = NW == 4 ? u == 1 : wave >= 4;
-            q64 = NW == 4 ? wave : (wave & 3);
-        } else {
-            is_b = wave >= 2;
-            q64 = wave & 1;
-        }
+        const int chunk = (wave + NW * u) % G::kScaleChunks;
+        const bool is_b = chunk >= TM / 64;
+        const int q64 = is_b ? chunk - TM / 64 : chunk;
         const int row = 64 * q64 + lane;
         s_src[u] = is_b ? bs : as;
         if constexpr (TILED) {
             // 64-row x 512-K scale blocks of 1024 bytes, 16 per row
-            s_off[u] = (uint32_t)(((is_b ? n0 : m0) / 64 + q64) * (K / 512) * 1024 + lane * 16);
+            s_off[u] = ((uint32_t)(is_b ? n0 : m0) / 64 + (uint32_t)q64) * ((uint32_t)K / 512) * 1024u +
+                       (uint32_t)lane * 16u;
         } else {
             s_off[u] = (uint32_t)(is_b ? min(n0 + row, N - 1) * ldbs : min(m0 + row, M - 1) * ldas);
         }
-        s_dst[u] = (is_b ? TILE * 16 : 0) + 1024 * q64;
+        s_dst[u] = (is_b ? TM * 16 : 0) + 1024 * q64;
     }
     // fragment and scale reads of this lane
     const int perm = chunk_perm(r);
@@ -355,28 +436,29 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TILE>::kMinBlocks)) void gemm_mxf
     const int chunk0 = 16 * ((0 + half) ^ perm);
     const int chunk1 = 16 * ((2 + half) ^ perm);
     const int sa_lds = kScaleBase + 16 * (wm * G::kWaveRows + r);
-    const int sb_lds = kScaleBase + 16 * (TILE + wn * G::kWaveCols + r);
+    const int sb_lds = kScaleBase + 16 * (TM + wn * G::kWaveCols + r);
 
     const int stage0 = split * (K / kStageK / splits);  // first stage of this split
     auto dma = [&](int buf, int stage) {
-        uint8_t *dst = lds + buf * kStageBytes + dma_row0 * kRowBytes;
+        uint8_t *dst = lds + buf * kStageBytes;
         const uint32_t step = TILED ? 1024u : (uint32_t)kRowBytes;
         const uint8_t *asrc = aq + (uint32_t)(stage0 + stage) * step;
         const uint8_t *bsrc = bq + (uint32_t)(stage0 + stage) * step;
 #pragma unroll
-        for (int u = 0; u < G::kDmaPerOperand; ++u)
+        for (int u = 0; u < G::kDmaA; ++u)
             __builtin_amdgcn_global_load_lds((gbl_void_t *)(asrc + a_off[u]),
-                                             (lds_void_t *)(dst + u * 1024), 16, 0, 0);
+                                             (lds_void_t *)(dst + a_row0 * kRowBytes + u * 1024), 16, 0, 0);
 #pragma unroll
-        for (int u = 0; u < G::kDmaPerOperand; ++u)
+        for (int u = 0; u < G::kDmaB; ++u)
             __builtin_amdgcn_global_load_lds((gbl_void_t *)(bsrc + b_off[u]),
-                                             (lds_void_t *)(dst + kABytes + u * 1024), 16, 0, 0);
+                                             (lds_void_t *)(dst + kABytes + b_row0 * kRowBytes + u * 1024), 16, 0,
+                                             0);
     };
     auto dma_scales = [&](int g) {
         uint8_t *dst = lds + kScaleBase + (g & 1) * kScaleSlot;
 #pragma unroll
         for (int u = 0; u < G::kDmaPerScales; ++u)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(s_src[u] + (TILED ? 1024 : 16) * (stage0 / 4 + g) + s_off[u]),
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(s_src[u] + (TILED ? 1024u : 16u) * (uint32_t)(stage0 / 4 + g) + s_off[u]),
                                              (lds_void_t *)(dst + s_dst[u]), 16, 0, 0);
     };
     auto read_frags = [&](int buf, int chunk, u32x4 (&fa)[FI], u32x4 (&fb)[FJ]) {
@@ -509,11 +591,31 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TILE>::kMinBlocks)) void gemm_mxf
     using T = std::true_type;
     using F = std::false_type;
 
+    // segmented accumulation: the sum of the finished segments, in K order
+    v16f seg_sum[FOLD ? FI : 1][FOLD ? FJ : 1];
+    if constexpr (FOLD) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) seg_sum[i][j] = v16f{};
+    }
+
     for (int g = 0; g + 1 < ngroups; ++g) {
         stage(g, I0(), WS(), T(), T());
         stage(g, I1(), WSS(), T(), F());
         stage(g, I2(), WSS(), T(), F());
         stage(g, I3(), WS(), T(), F());
+        if constexpr (FOLD) {
+            if ((g + 1) % fold_groups == 0) {
+#pragma unroll
+                for (int i = 0; i < FI; ++i)
+#pragma unroll
+                    for (int j = 0; j < FJ; ++j) {
+                        seg_sum[i][j] = seg_sum[i][j] + acc[i][j];
+                        acc[i][j] = v16f{};
+                    }
+            }
+        }
     }
     {
         const int g = ngroups - 1;
@@ -522,9 +624,16 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TILE>::kMinBlocks)) void gemm_mxf
         stage(g, I2(), W0(), F(), F());
         stage(g, I3(), WNone(), F(), F());
     }
+    if constexpr (FOLD) {
+        // the last segment joins the earlier ones
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) acc[i][j] = seg_sum[i][j] + acc[i][j];
+    }
 
     // epilogue: acc[i][j] register q * 4 + t of lane (r, half) is
-    // C[m0 + 128 wm + 32 i + r][n0 + kWaveCols wn + 32 j + 8 q + 4 half + t]. With split-K the
+    // C[m0 + kWaveRows wm + 32 i + r][n0 + kWaveCols wn + 32 j + 8 q + 4 half + t]. With split-K the
     // unscaled partial product goes to partials[split][M][N] (FP32, beta 0) instead.
     if (splits > 1) out = OutSpec{partials + (int64_t)split * M * N, N, 1.0f, 0.0f, 0};
     float *c = static_cast<float *>(out.c);
@@ -532,10 +641,10 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TILE>::kMinBlocks)) void gemm_mxf
     const float alpha = out.alpha;
     // split-K partials are FP32 whatever the variant: a bf16 variant decides per launch
     const bool bf16_now = EPI == kEpiBF16 && out.bf16;
-    const bool full_cols = n0 + TILE <= N && (bf16_now ? out_vector_ok<true>(out) : out_vector_ok<false>(out));
+    const bool full_cols = n0 + TN <= N && (bf16_now ? out_vector_ok<true>(out) : out_vector_ok<false>(out));
     if (full_cols) {
-        // stage each 32-row slice of this wavefront's 128 x kWaveCols result through LDS so that
-        // a store instruction writes whole rows (two rows of kWaveCols floats)
+        // stage each 32-row slice of this wavefront's kWaveRows x kWaveCols result through LDS so
+        // that a store instruction writes whole rows (64 / (kWaveCols / 4) rows of kWaveCols floats)
         constexpr int kEpiRow = G::kWaveCols * 4 + 16;   // bytes per staged row (padded)
         constexpr int kEpiWave = 32 * kEpiRow;           // one slice per wavefront
         constexpr int kLanesPerRow = G::kWaveCols / 4;   // 16-byte pieces per row
@@ -655,6 +764,9 @@ int gemm_splits(int64_t M, int64_t N, int64_t K)
     if (K % 512 != 0 || tiles > 32) return 1;
     int s = 1;
     while (s < 8 && tiles * s * 2 <= 256 && (K / 512) % (s * 2) == 0 && K / (512 * s * 2) >= 2) s *= 2;
+    // each split's chain (one rounding per 32 K) plus the fixed-order sum of the partials must
+    // stay within the rounding bound; otherwise one workgroup per tile with a segmented chain
+    if (s > 1 && K / 32 / s + s > kMaxDepth) return 1;
     return s;
 }
 
@@ -679,50 +791,69 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
     const bool pipelined = tiled || (K % 512 == 0 && K > 0 && scales_aligned && offsets_fit);
     if (!pipelined) {
         const dim3 sgrid((unsigned)((N + kTileN - 1) / kTileN), (unsigned)((M + kTileM - 1) / kTileM));
-        return launch(gemm_mxfp4_simple, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
-                      (int)M, (int)N, (int)K, out);
+        // two blocks per 64-wide step
+        const int fold_steps = chain_segment((K + 63) / 64, 2);
+        if (fold_steps > 0)
+            return launch(gemm_mxfp4_simple<true>, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs,
+                          ldbs, (int)M, (int)N, (int)K, out, fold_steps);
+        return launch(gemm_mxfp4_simple<false>, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
+                      (int)M, (int)N, (int)K, out, 0);
     }
     int splits = gemm_splits(M, N, K);
     if (splits > 1 && (workspace == nullptr || ws_bytes < gemm_workspace_bytes(M, N, K) ||
                        (uintptr_t)workspace % 16 != 0))
         splits = 1;
     float *partials = splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    // an unsplit contraction longer than one chain may be: segments of whole groups (16 blocks)
+    const int fold = splits == 1 ? chain_segment(K / 512, 16) : 0;
     hipError_t e;
-    if (splits == 1 && tiles_m * tiles_n <= kComputeUnits / 2) {
+    // pick one kernel variant by layout and epilogue (FOLD: segmented accumulation)
+    auto pick = [&](auto run_kernel, auto nw, auto tm, auto tn, auto wm, auto fold_v) {
+        constexpr int NW = decltype(nw)::value, TM = decltype(tm)::value, TN = decltype(tn)::value;
+        constexpr int WM = decltype(wm)::value;
+        constexpr bool FOLD = decltype(fold_v)::value;
+        if (tiled)
+            return epi == kEpiBF16 ? run_kernel(gemm_mxfp4_pipelined<NW, true, kEpiBF16, TM, TN, WM, FOLD>)
+                 : epi == kEpiF32Beta ? run_kernel(gemm_mxfp4_pipelined<NW, true, kEpiF32Beta, TM, TN, WM, FOLD>)
+                                      : run_kernel(gemm_mxfp4_pipelined<NW, true, kEpiF32, TM, TN, WM, FOLD>);
+        return epi == kEpiBF16 ? run_kernel(gemm_mxfp4_pipelined<NW, false, kEpiBF16, TM, TN, WM, FOLD>)
+             : epi == kEpiF32Beta ? run_kernel(gemm_mxfp4_pipelined<NW, false, kEpiF32Beta, TM, TN, WM, FOLD>)
+                                  : run_kernel(gemm_mxfp4_pipelined<NW, false, kEpiF32, TM, TN, WM, FOLD>);
+    };
+    using C4 = std::integral_constant<int, 4>;
+    using C2 = std::integral_constant<int, 2>;
+    using C128 = std::integral_constant<int, 128>;
+    using C256 = std::integral_constant<int, 256>;
+    if (splits == 1 && fold > 0 && tiles_m * tiles_n > kComputeUnits / 2) {
+        // segmented chains on a full grid: the 256 x 128 tile
+        const int mm = (int)((M + kFoldTM - 1) / kFoldTM), mn = (int)((N + kFoldTN - 1) / kFoldTN);
+        const auto run_mid = [&](auto kernel) {
+            return launch(kernel, dim3((unsigned)(mm * mn)), dim3(64 * kFoldWaves), 0, stream, aq, lda, as, ldas, bq,
+                          ldb, bs, ldbs, (int)M, (int)N, (int)K, out, mm, mn, 1, (float *)nullptr, fold);
+        };
+        return pick(run_mid, std::integral_constant<int, kFoldWaves>(), std::integral_constant<int, kFoldTM>(),
+                    std::integral_constant<int, kFoldTN>(), C4(), std::true_type());
+    }
+    if (splits == 1 && (fold > 0 || tiles_m * tiles_n <= kComputeUnits / 2)) {
         // 256 x 256 tiles would leave at least half the compute units idle: 128 x 128 tiles, four
         // wavefronts, two workgroups per CU, four times as many workgroups. Measured faster up to
         // 128 large tiles (8192 x 1024 x 4096: 28.2 -> 24.6 us; 1024 x 4096 x 8192: 45.9 -> 24.0 us)
         // and slower from 192 on (8192 x 1536 x 4096: 33.0 -> 35.2 us), where the small tiles'
         // doubled operand traffic costs more than the extra workgroups gain.
-        constexpr int kSmall = 128;
-        const int sm = (int)((M + kSmall - 1) / kSmall), sn = (int)((N + kSmall - 1) / kSmall);
+        const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
         const auto run_small = [&](auto kernel) {
             return launch(kernel, dim3((unsigned)(sm * sn)), dim3(64 * 4), 0, stream, aq, lda, as, ldas, bq, ldb, bs,
-                          ldbs, (int)M, (int)N, (int)K, out, sm, sn, 1, (float *)nullptr);
+                          ldbs, (int)M, (int)N, (int)K, out, sm, sn, 1, (float *)nullptr, fold);
         };
-        if (tiled)
-            e = epi == kEpiBF16 ? run_small(gemm_mxfp4_pipelined<4, true, kEpiBF16, kSmall>)
-              : epi == kEpiF32Beta ? run_small(gemm_mxfp4_pipelined<4, true, kEpiF32Beta, kSmall>)
-                                   : run_small(gemm_mxfp4_pipelined<4, true, kEpiF32, kSmall>);
-        else
-            e = epi == kEpiBF16 ? run_small(gemm_mxfp4_pipelined<4, false, kEpiBF16, kSmall>)
-              : epi == kEpiF32Beta ? run_small(gemm_mxfp4_pipelined<4, false, kEpiF32Beta, kSmall>)
-                                   : run_small(gemm_mxfp4_pipelined<4, false, kEpiF32, kSmall>);
-        return e;
+        if (fold > 0) return pick(run_small, C4(), C128(), C128(), C2(), std::true_type());
+        return pick(run_small, C4(), C128(), C128(), C2(), std::false_type());
     }
     const dim3 grid((unsigned)(tiles_m * tiles_n * splits)), block(64 * kGemmWaves);
     const auto run = [&](auto kernel) {
         return launch(kernel, grid, block, 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs, (int)M, (int)N, (int)K,
-                      out, tiles_m, tiles_n, splits, partials);
+                      out, tiles_m, tiles_n, splits, partials, 0);
     };
-    if (tiled)
-        e = epi == kEpiBF16 ? run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiBF16>)
-          : epi == kEpiF32Beta ? run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32Beta>)
-                               : run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32>);
-    else
-        e = epi == kEpiBF16 ? run(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiBF16>)
-          : epi == kEpiF32Beta ? run(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiF32Beta>)
-                               : run(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiF32>);
+    e = pick(run, std::integral_constant<int, kGemmWaves>(), C256(), C256(), C2(), std::false_type());
     if (e != hipSuccess || splits == 1) return e;
     const int64_t total = M * N;
     return launch(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
