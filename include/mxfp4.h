@@ -310,6 +310,22 @@ mxfp4_status_t mxfp4_linear_backward(const void *dy_bf16, int64_t M, int64_t K, 
                                      const mxfp4_step_cfg_t *cfg, void *ws, size_t ws_bytes,
                                      float *dx, float *dw, void *stream);
 
+/*
+ * mxfp4_linear_fprop without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, rules and result as mxfp4_linear_fprop (bitwise), except that the workspace is the
+ * library's own device array of MXFP4_NOALLOC_SCRATCH_BYTES bytes: one per GPU the library runs
+ * on, held until the process ends, looked up on the first call on each device. The call allocates
+ * nothing. Products whose mxfp4_linear_workspace_bytes(MXFP4_FPROP, M, K, N) exceeds the array
+ * return MXFP4_ERR_WORKSPACE before anything is launched (the Llama-3.1-8B QKV Fprop at 8192
+ * tokens needs 30 MB; the down projection's Fprop, 94 MB, is refused). Every call on one GPU
+ * shares its array: calls whose work overlaps on that GPU (other streams, other threads) race;
+ * calls ordered on one stream do not.
+ */
+#define MXFP4_NOALLOC_SCRATCH_BYTES (64u << 20)
+mxfp4_status_t mxfp4_linear_fprop_noalloc(const void *x_bf16, const void *w_bf16, int64_t M, int64_t K,
+                                          int64_t N, const mxfp4_linear_cfg_t *cfg, float *y, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *mxfp4_status_string(mxfp4_status_t status);
 

@@ -16,7 +16,7 @@ import torch  # imported first: the library binds to the HIP runtime torch has l
 __all__ = [
     "Mxfp4Error", "RHT", "ORTHO", "SCALE_NOCLIP", "quantize", "quantize_dual", "gemm", "linear_fprop",
     "linear_dgrad", "linear_wgrad", "linear_forward", "linear_backward", "step_workspace_bytes", "workspace_bytes", "library_path", "lib", "RNE", "SR", "FPROP", "DGRAD", "WGRAD", "ROWS", "TILED",
-    "tiled_sizes", "gemm_workspace_bytes",
+    "tiled_sizes", "gemm_workspace_bytes", "linear_fprop_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -99,6 +99,8 @@ def lib():
     L.mxfp4_linear_backward.argtypes = [vp, i64, i64, i64, ctypes.POINTER(StepCfg), vp, ctypes.c_size_t, vp, vp,
                                         vp]
     L.mxfp4_linear_backward.restype = ci
+    L.mxfp4_linear_fprop_noalloc.argtypes = [vp, vp, i64, i64, i64, ctypes.POINTER(LinearCfg), vp, vp]
+    L.mxfp4_linear_fprop_noalloc.restype = ci
     L.mxfp4_status_string.argtypes = [ci]
     L.mxfp4_status_string.restype = ctypes.c_char_p
     L.mxfp4_abi_version.argtypes = []
@@ -328,6 +330,31 @@ def linear_wgrad(dy, x, hadamard=16, rnd_a="rne", rnd_b="rne", seed=0, out=None,
     K = x.shape[1]
     return _linear("mxfp4_linear_wgrad", WGRAD, dy, x, M, K, N, (N, K), hadamard, rnd_a, rnd_b,
                    seed, out, workspace, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MXFP4_NOALLOC_SCRATCH_BYTES
+
+
+def linear_fprop_noalloc(x, w, hadamard=16, rnd_a="rne", rnd_b="rne", seed=0, out=None, stream=None):
+    """linear_fprop through mxfp4_linear_fprop_noalloc: the library's own per-device scratch array
+    instead of a workspace (products needing more than NOALLOC_SCRATCH_BYTES are refused). Calls
+    whose work overlaps on one GPU share that array and race."""
+    _require_cuda(x, "x")
+    _require_cuda(w, "w")
+    for t in (x, w):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError("linear operands must be contiguous bfloat16")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    cfg = LinearCfg(int(hadamard), _rounding(rnd_a), _rounding(rnd_b), int(seed) & (2 ** 64 - 1))
+    st = lib().mxfp4_linear_fprop_noalloc(x.data_ptr(), w.data_ptr(), M, K, N, ctypes.byref(cfg), out.data_ptr(),
+                                          _stream(stream))
+    _check(st, "mxfp4_linear_fprop_noalloc")
+    return out
 
 
 def step_workspace_bytes(M, K, N) -> int:

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp4.so")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "noalloc.hip"]
 HEADERS = ["internal.h", "mx_device.h"]
 CEILING_LIB = os.path.join(HERE, "libmxfp4_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]
