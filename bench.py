@@ -13,8 +13,11 @@ axis. This follows the gist.science summary "기술 요약: MXFP4 를 활용한 
 학습", section 방법론 (Methodology): all three GEMMs in MXFP4 behind the deterministic H16
 rotation; stochastic rounding on the weight-gradient operands is the full-layer recipe here.
 
-Default workload: the Llama-3.1-8B QKV projection, M = 8192 tokens, K = 4096, N = 6144,
-Fprop + Dgrad + Wgrad. `--workload layer` runs all 7 projections of one decoder layer.
+Default workload: one Llama-3.1-8B decoder layer at 8192 tokens, all 7 projections (q 4096->4096,
+k and v 4096->1024, o 4096->4096, gate and up 4096->14336, down 14336->4096) x Fprop + Dgrad +
+Wgrad, H16, nearest rounding for Fprop and Dgrad and Philox stochastic rounding on both Wgrad
+operands: 21 GEMMs per step. `--workload qkv` runs the QKV projection alone (M = 8192, K = 4096,
+N = 6144), `small`, `gateup` and `down` the other single-projection configurations.
 Prints ONE JSON line. Inputs are resident in HBM before the timed region starts.
 """
 import argparse
@@ -52,7 +55,7 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=sorted(WORKLOADS), default="qkv")
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default="layer")
     p.add_argument("--hadamard", type=int, default=16, choices=[0, 16, 32])
     p.add_argument("--rht", action="store_true",
                    help="randomized Hadamard: a sign diagonal keyed by each GEMM's seed before H")
@@ -60,7 +63,8 @@ def parse_args():
     p.add_argument("--settle", type=float, default=1.0,
                    help="seconds of untimed steps before the warm-up (GPU clock ramp)")
     p.add_argument("--no-library-baselines", action="store_true",
-                   help="skip the vendor GEMM baselines (hipBLASLt MXFP8 / MXFP4 / FP8 / bf16)")
+                   help="skip the vendor GEMM baselines (hipBLASLt FP8 per tensor and MXFP8 at every GEMM "
+                        "shape of the step, on the step's operands)")
     p.add_argument("--separate-quant", action="store_true",
                    help="one quantizer launch per axis instead of one dual launch per tensor")
     p.add_argument("--no-ceilings", action="store_true",
@@ -243,30 +247,81 @@ class Plan:
         return calls
 
 
-def measured_traffic(workload):
-    """HBM bytes per GEMM launch from the committed counter summary, if it was taken on the QKV
-    step with the GEMM source as it is now (otherwise None)."""
+def _profile_values(name, source):
+    """key: value lines and table rows of a committed counter summary under profiles/, if it was
+    taken with `source` (a file of the HIP library) as it is now; otherwise None."""
     import hashlib
-    if workload != "qkv":
-        return None
-    path = os.path.join(ROOT, "profiles", "gemm_mxfp4_qkv_step_hbm_bytes.txt")
-    src = os.path.join(ROOT, "mxfp4_block_scaled_h16_amd", "csrc", "gemm.hip")
+    path = os.path.join(ROOT, "profiles", name)
+    src = os.path.join(ROOT, "mxfp4_block_scaled_h16_amd", "csrc", source)
     if not os.path.exists(path):
         return None
-    vals = {}
+    vals, rows = {}, []
     with open(path) as f:
         for line in f:
-            if ":" in line and not line.startswith("#"):
+            if line.startswith("#") or not line.strip():
+                continue
+            if "|" in line:
+                rows.append([c.strip() for c in line.split("|")])
+            elif ":" in line:
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     with open(src, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()[:16]
-    if vals.get("gemm_source_digest") != digest:
+    if vals.get("source_digest") != digest:
+        return None
+    return vals, rows
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch of the step, averaged over its GEMM launches, from the committed
+    FETCH_SIZE / WRITE_SIZE summary of this workload, if it was taken with the GEMM source as it
+    is now (otherwise None)."""
+    got = _profile_values("gemm_mxfp4_%s_step_hbm_bytes.txt" % workload, "gemm.hip")
+    if got is None:
         return None
     try:
-        return float(vals["traffic_bytes_per_launch"])
+        return float(got[0]["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9   # CUs x SIMDs x lanes x clock: 39.3 T lane-ops/s
+
+
+def quantizer_valu(workload, plan, avg_ms):
+    """The stochastic-rounding quantizer launches against the VALU roofline: VALU instructions
+    per wavefront and wavefronts per launch from the committed SQ counter summary of this
+    workload (taken with the quantizer source as it is now, else None), times 64 lanes, over the
+    launch's duration in this run, against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz. Counts every
+    VALU instruction as one issue per 16 lanes (the 64-bit multiply-adds of Philox take longer,
+    so the VALU is busier than this says)."""
+    got = _profile_values("quant_%s_step_sq_counters.txt" % workload, "quantize.hip")
+    if got is None:
+        return None
+    counts = {}
+    for row in got[1]:
+        if len(row) >= 3 and row[0] not in ("launch", ""):
+            try:
+                counts[row[0]] = (float(row[1]), float(row[2]))   # waves, VALU instructions per wave
+            except ValueError:
+                pass
+    launches, ops_total, t_total = {}, 0.0, 0.0
+    for (label, kind, spec, _), t in zip(plan.op_list, avg_ms):
+        if kind != "dual" or label not in counts:
+            continue
+        if not any(q[4] == "sr" for q in spec):
+            continue
+        waves, per_wave = counts[label]
+        ops = waves * per_wave * 64
+        launches[label] = {"valu_giga_lane_ops": round(ops / 1e9, 2),
+                           "frac": round(ops / (float(t) * 1e-3) / VALU_LANE_OPS_PEAK, 4)}
+        ops_total += ops
+        t_total += float(t) * 1e-3
+    if not launches:
+        return None
+    return {"bound": "valu", "achieved": round(ops_total / t_total / 1e12, 2), "peak": round(VALU_LANE_OPS_PEAK / 1e12, 2),
+            "unit": "T lane-ops/s", "frac": round(ops_total / t_total / VALU_LANE_OPS_PEAK, 4),
+            "launches": launches, "counters": "profiles/quant_%s_step_sq_counters.txt" % workload}
 
 
 def quantization_error(plan, rows=8):
@@ -542,48 +597,90 @@ def step_entry_points(plan, steps, warmup, settle_s=0.25):
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
 
 
-def library_baselines(M, N, K, steps, settle_s=0.25):
-    """Vendor GEMMs (hipBLASLt through torch._scaled_mm / torch.mm) at one product shape, as
-    context: block-scaled MXFP8 and MXFP4 (E8M0 scale per 32 along K), per-tensor FP8 and
-    bf16. The block-scaled paths accept only bf16/fp16 outputs, so they write half the output
-    bytes this library's FP32 GEMM writes. Operands are random codes with scales near 1.
-    Each is settled for `settle_s` seconds, then timed over K launches (host clock)."""
+def gemm_operands_bf16(plan, okey):
+    """The bf16 device operands (A [rows_A, Kc], B [rows_B, Kc], both contiguous) of one GEMM of
+    the plan, from its first input set: Fprop A = X, B = W; Dgrad A = dY, B = W^T; Wgrad A = dY^T,
+    B = X^T."""
+    name, pas = okey
+    d_acts, d_proj = plan.sets[0]
+    w, dy = d_proj[name]
+    key = LLAMA_INPUT.get(name)
+    x = d_acts[key] if key in d_acts else d_acts["x"]
+    if pas == "F":
+        return x, w
+    if pas == "D":
+        return dy, w.t().contiguous()
+    return dy.t().contiguous(), x.t().contiguous()
+
+
+def fp8_per_tensor(t):
+    """FP8 E4M3 codes of t with one binary32 scale: amax / 448 (the largest E4M3 value)."""
     import torch
-    dev = "cuda"
-    g = torch.Generator(device=dev).manual_seed(0)
-    e8 = lambda rows: torch.randint(124, 131, (rows, K // 32), dtype=torch.uint8, device=dev,  # noqa: E731
-                                    generator=g).view(torch.float8_e8m0fnu)
-    a8 = torch.randn(M, K, device=dev, generator=g).to(torch.float8_e4m3fn)
-    b8 = torch.randn(N, K, device=dev, generator=g).to(torch.float8_e4m3fn)
-    a4 = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=g).view(torch.float4_e2m1fn_x2)
-    b4 = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g).view(torch.float4_e2m1fn_x2)
-    sa, sb = e8(M), e8(N)
-    one = torch.tensor(1.0, device=dev)
-    abf = torch.randn(M, K, device=dev, generator=g, dtype=torch.bfloat16)
-    bbf = torch.randn(N, K, device=dev, generator=g, dtype=torch.bfloat16)
-    cases = {
-        "hipblaslt_mxfp8_e4m3": lambda: torch._scaled_mm(a8, b8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
-        "hipblaslt_mxfp4": lambda: torch._scaled_mm(a4, b4.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
-        "hipblaslt_fp8_e4m3_per_tensor": lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,
-                                                                  out_dtype=torch.bfloat16),
-        "hipblaslt_bf16": lambda: torch.mm(abf, bbf.t()),
-    }
-    out = {"shape": "M=%d N=%d K=%d" % (M, N, K), "output": "bf16"}
-    for name, f in cases.items():
-        try:
-            t_end = time.perf_counter() + settle_s
-            while time.perf_counter() < t_end:
-                f()
+    amax = t.float().abs().max().clamp(min=1e-30)
+    scale = (amax / 448.0).float()
+    return (t.float() / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn), scale
+
+
+def mxfp8(t):
+    """MXFP8 (E4M3 elements, one E8M0 scale per 32 along the rows): the shared exponent is
+    floor(log2 amax) - 8 (the largest E4M3 exponent), elements saturate at 448."""
+    import torch
+    rows, kc = t.shape
+    blk = t.float().reshape(rows, kc // 32, 32)
+    amax = blk.abs().amax(-1).clamp(min=2.0 ** -126)
+    e = torch.floor(torch.log2(amax)) - 8
+    e = e.clamp(-127, 127)
+    codes = (blk / torch.exp2(e)[..., None]).clamp(-448.0, 448.0).reshape(rows, kc).to(torch.float8_e4m3fn)
+    return codes, (e + 127).to(torch.uint8).view(torch.float8_e8m0fnu)
+
+
+def vendor_gemm(kind, a, b):
+    """The vendor (hipBLASLt) product A B^T in bf16 for FP8 operands of fp8_per_tensor ("fp8") or
+    mxfp8 ("mxfp8"); a and b are (codes, scale) pairs."""
+    import torch
+    return torch._scaled_mm(a[0], b[0].t(), scale_a=a[1], scale_b=b[1], out_dtype=torch.bfloat16)
+
+
+def library_baselines(plan, avg_ms, steps, settle_s=0.1):
+    """Vendor GEMMs (hipBLASLt through torch._scaled_mm) at every GEMM shape of the step, on the
+    step's own operands converted to FP8 E4M3 once, outside timing: per-tensor FP8 and MXFP8
+    (E8M0 scale per 32). The FP8 form of the method's step is the pages' baseline; these are its
+    GEMMs alone (bf16 output, half the bytes of this library's FP32 output). Each shape is
+    settled for `settle_s` seconds, then timed over K launches (host clock)."""
+    import torch
+    out = {"output": "bf16", "operands": "the step's bf16 operands, converted once outside timing", "gemms": {}}
+    ours_s, tot = 0.0, {"fp8_per_tensor": 0.0, "mxfp8": 0.0}
+    for (label, kind, spec, work), t in zip(plan.op_list, avg_ms):
+        if kind != "gemm":
+            continue
+        A, B = gemm_operands_bf16(plan, spec[2])
+        entry = {"shape": "%dx%dx%d" % (A.shape[0], B.shape[0], A.shape[1]),
+                 "this_library_us": round(float(t) * 1e3, 2)}
+        ours_s += float(t) * 1e-3
+        for name, conv, vk in (("fp8_per_tensor", fp8_per_tensor, "fp8"), ("mxfp8", mxfp8, "mxfp8")):
+            try:
+                a, b = conv(A), conv(B)
+                f = lambda a=a, b=b, vk=vk: vendor_gemm(vk, a, b)  # noqa: E731
+                t_end = time.perf_counter() + settle_s
+                while time.perf_counter() < t_end:
+                    f()
+                    torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    f()
                 torch.cuda.synchronize()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(steps):
-                f()
-            torch.cuda.synchronize()
-            us = (time.perf_counter() - t0) * 1e6 / steps
-            out[name] = {"us": round(us, 2), "tflops": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1)}
-        except Exception as e:  # a baseline the runtime does not offer is reported, not fatal
-            out[name] = {"error": str(e)[:200]}
+                us = (time.perf_counter() - t0) * 1e6 / steps
+                entry[name + "_us"] = round(us, 2)
+                tot[name] += us * 1e-6
+                del a, b
+            except Exception as e:  # a baseline the runtime does not offer is reported, not fatal
+                entry[name + "_error"] = str(e)[:160]
+                tot[name] = float("nan")
+        del A, B
+        out["gemms"][label] = entry
+    out["step_gemm_ms"] = {"this_library_mxfp4": round(ours_s * 1e3, 4),
+                           "fp8_per_tensor": round(tot["fp8_per_tensor"] * 1e3, 4),
+                           "mxfp8": round(tot["mxfp8"] * 1e3, 4)}
     return out
 
 
@@ -663,12 +760,11 @@ def main():
     entry = step_entry_points(plan, args.steps, args.warmup) if args.workload == "qkv" else None
 
     baselines = None
-    if args.workload == "qkv" and not args.no_library_baselines:
-        baselines = library_baselines(M, projs[0][2], projs[0][1], args.steps)
-        gemm_f = next(t for (label, kind, _, _), t in zip(plan.op_list, avg_ms) if label.startswith("gemm Fprop"))
-        baselines["this_library_mxfp4_fp32_output"] = {"us": round(float(gemm_f) * 1e3, 2),
-                                                       "tflops": round(2.0 * M * projs[0][2] * projs[0][1]
-                                                                       / (float(gemm_f) * 1e-3) / 1e12, 1)}
+    if not args.no_library_baselines and passes == "FDW":
+        baselines = library_baselines(plan, avg_ms, args.steps)
+    valu = quantizer_valu(args.workload, plan, avg_ms)
+    if valu is not None:
+        quantizer["valu"] = valu
 
     if args.copy_calibration:
         buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

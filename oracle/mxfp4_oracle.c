@@ -56,12 +56,14 @@
  *
  * Pins (tests/test_oracle_pins.py, no GPU): the E2M1 value table and nearest-even tie points,
  * the scale rule's closed form, the Hadamard matrix and its identities, round-trip bounds,
- * exact constructions and rational brute force for the GEMM and both roundings, and the
- * published Philox4x32-10 known-answer vectors. Parity unpinned: the conventions the pages leave
- * open and that no outside fact can fix -- the sign bit of zero codes, the nibble order, the
- * Philox key / counter / word assignment of the stochastic rounding, and the sign sequence of
- * the randomized rotation (its use, signs then H, is pinned by an exact construction). Only
- * agreement between this oracle and the GPU checks them.
+ * exact constructions and rational brute force for the GEMM and both roundings, the published
+ * Philox4x32-10 known-answer vectors, and the stochastic rounding's word choice and key through
+ * the published zero-counter block (elements 0..3 of row 0 under seed 0, stream 0 decide with its
+ * four words). Parity unpinned: the conventions the pages leave open and that no outside fact can
+ * fix -- the sign bit of zero codes, the nibble order, which counter words carry the index's high
+ * bits and the stream (zero in the published block), and the sign sequence of the randomized
+ * rotation (its use, signs then H, is pinned by an exact construction). Only agreement between
+ * this oracle and the GPU checks them.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC (see build.py).
  * OpenMP splits only the outermost loop over independent rows; per-row arithmetic is sequential.

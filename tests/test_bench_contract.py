@@ -46,3 +46,43 @@ def test_cpu_baseline_leg_on_a_small_plan():
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
     assert r["value"] > 0 and r["gemm_gflops"] > 0 and r["cpu_seconds"] >= 0
     assert "output rows" in r["sample"] and np.isfinite(r["step_seconds_projected"])
+
+
+def test_default_workload_is_the_decoder_layer():
+    """The benchmark's headline runs one Llama-3.1-8B decoder layer (7 projections x Fprop, Dgrad,
+    Wgrad: 21 GEMMs) unless told otherwise."""
+    sys.path.insert(0, ROOT)
+    import bench
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        args = bench.parse_args()
+    finally:
+        sys.argv = old
+    assert args.workload == "layer" and args.gpus == 1
+    desc, projs, passes, M = bench.WORKLOADS["layer"]
+    assert passes == "FDW" and M == 8192 and len(projs) == 7
+
+
+def test_counter_summaries_are_ignored_once_the_source_changes(tmp_path, monkeypatch):
+    """Traffic and VALU figures come from committed counter summaries only while the kernel source
+    has the digest recorded in them."""
+    import hashlib
+    import types
+    sys.path.insert(0, ROOT)
+    import bench
+    prof = tmp_path / "profiles"
+    src = tmp_path / "mxfp4_block_scaled_h16_amd" / "csrc"
+    prof.mkdir()
+    src.mkdir(parents=True)
+    (src / "quantize.hip").write_text("// kernel v1\n")
+    digest = hashlib.sha256(b"// kernel v1\n").hexdigest()[:16]
+    (prof / "quant_layer_step_sq_counters.txt").write_text(
+        "# test\nsource_digest: %s\nlaunch | waves | valu_per_wave\nquant_dual x | 100 | 2000\n" % digest)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    plan = types.SimpleNamespace(op_list=[("quant_dual x", "dual", ((0, 0, 0, 1, "rne"), (0, 0, 0, 0, "sr")), 0)])
+    v = bench.quantizer_valu("layer", plan, [0.01])
+    assert v["launches"]["quant_dual x"]["valu_giga_lane_ops"] == round(100 * 2000 * 64 / 1e9, 2)
+    assert abs(v["frac"] - 100 * 2000 * 64 / 1e-5 / bench.VALU_LANE_OPS_PEAK) < 1e-3
+    (src / "quantize.hip").write_text("// kernel v2\n")
+    assert bench.quantizer_valu("layer", plan, [0.01]) is None

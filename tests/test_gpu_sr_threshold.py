@@ -112,3 +112,25 @@ def test_dual_kernel(case):
     _same(host(q0), host(s0), q, s, "dual, transposed output")
     rq, rs = oracle.quantize(xt, axis=1, hadamard=0, rounding=oracle.SR, seed=SEED, stream=0)
     _same(host(q1), host(s1), rq, rs, "dual, row output")
+
+
+@pytest.mark.parametrize("d", [0, 1])
+def test_published_zero_counter_block_in_every_kernel(d):
+    """Seed 0, stream 0: the first four elements of quantized row 0 decide with the published
+    Philox4x32-10 output words of counter 0 and key 0 (Salmon et al.), read from
+    tests/golden/philox4x32_10_kat.txt, with no oracle involved: on their own word's threshold
+    they round down, one 2^-22 unit above it they round up, in the row, column and dual kernels."""
+    import mxfp4_block_scaled_h16_amd as mx
+    from tests.test_oracle_pins import sr_kat_probe
+    row, want = sr_kat_probe(d)
+    x = np.zeros((32, 32), dtype=np.float32)
+    x[:, 31] = 4.0
+    x[0] = row[0]
+    xt = np.ascontiguousarray(x.T)
+    announce("sr published block, d =", d)
+    gq, gs = mx.quantize(f32_dev(x), axis=1, hadamard=0, rounding="sr", seed=0, stream_id=0)
+    cq, cs = mx.quantize(f32_dev(xt), axis=0, hadamard=0, rounding="sr", seed=0, stream_id=0)
+    _, _, dq, ds = mx.quantize_dual(f32_dev(xt), 0, dict(rounding="rne"), dict(rounding="sr", seed=0, stream_id=0))
+    for name, q, s in (("rows", gq, gs), ("cols", cq, cs), ("dual", dq, ds)):
+        assert host(s)[0, 0] == 127, name
+        assert list(_unpack(host(q))[0, :4]) == want, name

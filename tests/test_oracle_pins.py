@@ -350,6 +350,36 @@ def test_sr_threshold_22_bits():
         assert codes[o, j] == expect
 
 
+def sr_kat_probe(d):
+    """One 32-element row for the stochastic-rounding pin by the published zero-counter block:
+    elements 0..3 sit at the rounding threshold of the top 22 bits of the Philox4x32-10 output
+    words 0..3 for counter 0 and key 0 (tests/golden/philox4x32_10_kat.txt, first row), plus d
+    units of 2^-23; element 31 is 4.0 so that the block's scale is 2^0 and the grid step below
+    0.5 is 0.5. Returns (x, the expected magnitude codes of elements 0..3)."""
+    words = [int(w, 16) for w in read_golden("philox4x32_10_kat.txt")[0][6:10]]
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 31] = 4.0
+    for j, w in enumerate(words):
+        x[0, j] = np.float32(((w >> 10) + d) * 2.0 ** -23)
+        assert float(x[0, j]) == ((w >> 10) + d) * 2.0 ** -23
+    # |v| = (r22 + d) 2^-23 below 0.5: f = |v| / 0.5, floor(2^22 f) = r22 + d, rounds up iff
+    # r22 < r22 + d
+    return x, [1 if d >= 1 else 0] * 4
+
+
+@pytest.mark.parametrize("d", [0, 1])
+def test_sr_words_follow_published_zero_counter_block(d):
+    """With seed 0 and stream 0, the first four elements of row 0 draw words 0, 1, 2, 3 of
+    Philox4x32-10 at counter 0 and key 0, whose values are published (Salmon et al.): each
+    element placed exactly on its own word's threshold rounds down, one 2^-22 unit above it rounds
+    up. A swapped word, a per-element counter or a wrong key moves some element's threshold and
+    fails one of the two cases."""
+    x, want = sr_kat_probe(d)
+    q, s = oracle.quantize(x, axis=1, hadamard=0, rounding=oracle.SR, seed=0, stream=0)
+    assert s[0, 0] == 127
+    assert list(unpack_codes(q)[0, :4]) == want
+
+
 def test_sr_unbiased_and_noisier_than_rne():
     """Mean of SR over many seeds equals the value (5 sigma); MSE(SR) >= MSE(RNE)."""
     rng = np.random.default_rng(10)
