@@ -52,10 +52,17 @@
 extern "C" {
 #endif
 
-/* Raised whenever an entry point, a struct or the bits an entry point produces change. 9: the
+/* Raised whenever an entry point, a struct or the bits an entry point produces change. 10:
+ * mxfp4_linear_fprop_noalloc; GEMMs whose contraction exceeds 5120 accumulate in fixed segments
+ * (their FP32 results differ from 9 in the last bits); every enum spans the int32 range. 9: the
  * stochastic-rounding decision compares 22 random bits with the fractional position truncated to
  * 22 bits (codes for |v| < 1 differ from 8). */
-#define MXFP4_ABI_VERSION 9
+#define MXFP4_ABI_VERSION 10
+
+/* Every enum below includes the whole int32 range (the _RANGE_ members are not values to pass):
+ * an entry point receives whatever integer a C caller passes and refuses the ones it does not
+ * define with MXFP4_ERR_ARG, which in C++ is only well defined when the enum type can hold it. */
+#define MXFP4_ENUM_RANGE(prefix) prefix##_RANGE_MIN_ = -0x7FFFFFFF - 1, prefix##_RANGE_MAX_ = 0x7FFFFFFF
 
 typedef enum {
     MXFP4_OK = 0,
@@ -65,12 +72,13 @@ typedef enum {
     MXFP4_ERR_ALIGN = 4,     /* pointer or leading dimension misaligned (see each call) */
     MXFP4_ERR_WORKSPACE = 5, /* workspace smaller than mxfp4_linear_workspace_bytes() */
     MXFP4_ERR_DEVICE = 6,    /* no current HIP device, or it is not gfx950 */
-    MXFP4_ERR_LAUNCH = 7     /* the HIP runtime reported a launch error */
+    MXFP4_ERR_LAUNCH = 7,    /* the HIP runtime reported a launch error */
+    MXFP4_ENUM_RANGE(MXFP4_STATUS)
 } mxfp4_status_t;
 
-typedef enum { MXFP4_IN_BF16 = 0, MXFP4_IN_F32 = 1 } mxfp4_dtype_t;
+typedef enum { MXFP4_IN_BF16 = 0, MXFP4_IN_F32 = 1, MXFP4_ENUM_RANGE(MXFP4_DTYPE) } mxfp4_dtype_t;
 
-typedef enum { MXFP4_RNE = 0, MXFP4_SR_PHILOX = 1 } mxfp4_rounding_t;
+typedef enum { MXFP4_RNE = 0, MXFP4_SR_PHILOX = 1, MXFP4_ENUM_RANGE(MXFP4_ROUNDING) } mxfp4_rounding_t;
 
 /*
  * Scale variant: OR into a rounding value (quantize, quantize_dual, linear cfg rnd_a / rnd_b) to
@@ -81,7 +89,7 @@ typedef enum { MXFP4_RNE = 0, MXFP4_SR_PHILOX = 1 } mxfp4_rounding_t;
  */
 #define MXFP4_SCALE_NOCLIP 0x10
 
-typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
+typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2, MXFP4_ENUM_RANGE(MXFP4_PASS) } mxfp4_pass_t;
 
 /*
  * Randomized Hadamard: OR this flag into a hadamard size of 16 or 32 (quantize, quantize_dual,
@@ -123,7 +131,7 @@ typedef enum { MXFP4_FPROP = 0, MXFP4_DGRAD = 1, MXFP4_WGRAD = 2 } mxfp4_pass_t;
  *   Every 16-row x 128-element slice of codes and every 64-row x 512-element slice of scales is
  *   one contiguous kilobyte. Both pointers must be 16-byte aligned; ldq and lds are not used.
  */
-typedef enum { MXFP4_LAYOUT_ROWS = 0, MXFP4_LAYOUT_TILED = 1 } mxfp4_layout_t;
+typedef enum { MXFP4_LAYOUT_ROWS = 0, MXFP4_LAYOUT_TILED = 1, MXFP4_ENUM_RANGE(MXFP4_LAYOUT) } mxfp4_layout_t;
 
 /* Bytes of codes and of scales of a tiled operand (outer rows, length L); MXFP4_ERR_SHAPE if
  * L % 512 != 0 or a size is negative, MXFP4_ERR_NULL if an output pointer is NULL. */
@@ -209,7 +217,7 @@ mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int
                           mxfp4_layout_t layout, void *workspace, size_t ws_bytes, void *stream);
 
 /* Output element type of mxfp4_gemm_ex. */
-typedef enum { MXFP4_OUT_F32 = 0, MXFP4_OUT_BF16 = 1 } mxfp4_out_dtype_t;
+typedef enum { MXFP4_OUT_F32 = 0, MXFP4_OUT_BF16 = 1, MXFP4_ENUM_RANGE(MXFP4_OUT) } mxfp4_out_dtype_t;
 
 /*
  * mxfp4_gemm_ex -- mxfp4_gemm with an epilogue: c = alpha * A B^T + beta * c.

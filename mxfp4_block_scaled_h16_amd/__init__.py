@@ -235,6 +235,39 @@ def quantize_dual(x, hadamard=16, axis1=None, axis0=None, stream=None):
     return q1, s1, q0, s0
 
 
+def _check_gemm_operands(aq, as_, bq, bs, M, N, K, lay):
+    """Raise ValueError unless the operand tensors hold what an M x N x K product reads: codes
+    [rows][K/2] and scales [rows][K/32] with rows >= M (A) and >= N (B), rounded up to 256 for
+    the tiled layout (whose buffers are flat or [rows][...])."""
+    if M < 0 or N < 0:
+        raise ValueError("negative output size")
+    for t, nm in ((aq, "aq"), (as_, "as"), (bq, "bq"), (bs, "bs")):
+        if t.dtype != torch.uint8:
+            raise TypeError("%s must be uint8" % nm)
+        if t.stride(-1) != 1:
+            raise ValueError("%s must have unit column stride" % nm)
+    if lay == TILED:
+        pm, pn = (M + 255) // 256 * 256, (N + 255) // 256 * 256
+        for t, nm, rows, width in ((aq, "aq", pm, K // 2), (bq, "bq", pn, K // 2), (as_, "as", pm, K // 32),
+                                   (bs, "bs", pn, K // 32)):
+            if t.numel() < rows * width:
+                raise ValueError("%s holds %d bytes; the tiled %d x %d operand needs %d" % (nm, t.numel(), rows, K,
+                                                                                            rows * width))
+        return
+    if aq.dim() != 2 or bq.dim() != 2 or as_.dim() != 2 or bs.dim() != 2:
+        raise ValueError("row-major operands must be 2-D")
+    if bq.shape[1] * 2 != K:
+        raise ValueError("aq and bq disagree on K (%d vs %d)" % (K, bq.shape[1] * 2))
+    if K % 32:
+        raise ValueError("K = %d is not a multiple of 32" % K)
+    if as_.shape[1] != K // 32 or bs.shape[1] != K // 32:
+        raise ValueError("scales must have K/32 = %d columns" % (K // 32))
+    if aq.shape[0] < M or as_.shape[0] < M:
+        raise ValueError("A operand has fewer than M = %d rows" % M)
+    if bq.shape[0] < N or bs.shape[0] < N:
+        raise ValueError("B operand has fewer than N = %d rows" % N)
+
+
 def gemm_workspace_bytes(M, N, K) -> int:
     return int(lib().mxfp4_gemm_workspace_bytes(int(M), int(N), int(K)))
 
@@ -256,6 +289,7 @@ def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None, layout="rows", m=Non
         M, N = out.shape
     M = M if m is None else int(m)
     N = N if n is None else int(n)
+    _check_gemm_operands(aq, as_, bq, bs, M, N, K, lay)
     if out is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an existing `out`")

@@ -63,5 +63,39 @@ def build(force: bool = True, verbose: bool = False) -> str:
     return LIB
 
 
+BUILD_DIR = os.path.join(HERE, "..", "_build")
+
+
+def build_host_sanitized(verbose: bool = False):
+    """A copy of libmxfp4.so whose HOST code carries AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code is built as usual), plus tests/abi_validation.c
+    linked against it: a host-only driver of the C ABI's argument validation. Both go to _build/.
+    Returns the driver's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    lib = os.path.abspath(os.path.join(BUILD_DIR, "libmxfp4_hostsan.so"))
+    drv = os.path.abspath(os.path.join(BUILD_DIR, "abi_validation"))
+    driver_src = os.path.join(HERE, "..", "tests", "abi_validation.c")
+    if os.path.exists(drv) and os.path.exists(lib):
+        t = min(os.path.getmtime(drv), os.path.getmtime(lib))
+        if all(os.path.getmtime(f) <= t for f in _inputs() + [driver_src, __file__]):
+            return drv
+    host_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    cmd = [hipcc()] + HIPCC_FLAGS + host_san + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", lib]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    cmd = [clang, "-std=c11", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", driver_src, lib,
+           "-Wl,-rpath," + os.path.dirname(lib), "-o", drv]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return drv
+
+
 if __name__ == "__main__":
     print(build(force="--if-stale" not in sys.argv, verbose=True))

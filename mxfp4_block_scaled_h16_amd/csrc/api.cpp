@@ -140,6 +140,7 @@ bool pass_operands(mxfp4_pass_t pass, int64_t M, int64_t K, int64_t N, OperandSp
     case MXFP4_FPROP: *a = {M, K}; *b = {N, K}; return true;   // X along K, W along K
     case MXFP4_DGRAD: *a = {M, N}; *b = {K, N}; return true;   // dY along N, W^T along N
     case MXFP4_WGRAD: *a = {N, M}; *b = {K, M}; return true;   // dY^T along M, X^T along M
+    default: break;
     }
     return false;
 }
@@ -494,6 +495,7 @@ const char *mxfp4_status_string(mxfp4_status_t status)
     case MXFP4_ERR_WORKSPACE: return "workspace missing or too small";
     case MXFP4_ERR_DEVICE: return "no current gfx950 device";
     case MXFP4_ERR_LAUNCH: return "kernel launch failed";
+    default: break;
     }
     return "unknown status";
 }

@@ -12,16 +12,26 @@ SRC = os.path.join(HERE, "mxfp4_oracle.c")
 LIB = os.path.join(HERE, "libmxfp4_oracle.so")
 
 
-def build(force: bool = True) -> str:
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
-        return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
+SANITIZED_LIB = os.path.join(HERE, "..", "_build", "libmxfp4_oracle_san.so")
+
+
+def build(force: bool = True, sanitized: bool = False) -> str:
+    """Build the oracle library; sanitized=True builds a copy with AddressSanitizer and
+    UndefinedBehaviorSanitizer (every UB report fatal) under _build/, for test runs that preload
+    gcc's sanitizer runtimes."""
+    lib = os.path.abspath(SANITIZED_LIB) if sanitized else LIB
+    if not force and os.path.exists(lib) and os.path.getmtime(lib) >= os.path.getmtime(SRC):
+        return lib
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
+    tmp = lib + ".tmp%d" % os.getpid()
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"] \
+        if sanitized else []
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-fno-unsafe-math-optimizations", "-fPIC", "-shared", "-Wall", "-Wextra",
-           SRC, "-o", tmp, "-lm"]
+           "-fno-unsafe-math-optimizations", "-fPIC", "-shared", "-Wall", "-Wextra"] + san + \
+          [SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -63,7 +63,7 @@ def test_ceiling_library_exports_its_declared_symbols():
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 9
+    assert L.mxfp4_abi_version() == 10
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -260,3 +260,33 @@ def test_step_argument_errors(L):
     assert f(None, None, 0, 0, 0, ctypes.byref(ok), None, 0, None, None) == 0
     assert b(None, 0, 0, 0, ctypes.byref(ok), None, 0, None, None, None) == 0
 
+
+
+def test_gemm_binding_checks_operand_shapes():
+    """The binding refuses operands smaller than the product it is asked for (before any call
+    into the library): too few rows for M or N, K disagreeing between A and B or with the
+    scales, and tiled buffers shorter than their padded size. Runs on the CPU: the checks raise
+    before the device check."""
+    import torch
+    import mxfp4_block_scaled_h16_amd as mx
+
+    class FakeCuda(torch.Tensor):
+        """A CPU tensor that passes the binding's device check (the checks here raise first)."""
+        @property
+        def is_cuda(self):
+            return True
+
+    def t(*shape):
+        return torch.zeros(shape, dtype=torch.uint8).as_subclass(FakeCuda)
+
+    out = torch.empty((64, 32), dtype=torch.float32).as_subclass(FakeCuda)
+    cases = [
+        (t(32, 64), t(32, 4), t(32, 64), t(32, 4), dict(out=out)),            # A rows < M = 64
+        (t(64, 64), t(64, 4), t(16, 64), t(16, 4), dict(out=out)),            # B rows < N = 32
+        (t(64, 64), t(64, 4), t(32, 32), t(32, 2), dict(out=out)),            # K disagrees
+        (t(64, 64), t(64, 2), t(32, 64), t(32, 4), dict(out=out)),            # A scales != K/32
+        (t(256, 256), t(256, 16), t(256, 256), t(256, 16), dict(m=300, n=32, layout="tiled")),  # A not padded
+    ]
+    for aq, as_, bq, bs, kw in cases:
+        with pytest.raises(ValueError):
+            mx.gemm(aq, as_, bq, bs, **kw)
