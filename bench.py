@@ -272,6 +272,12 @@ def _profile_values(name, source):
     return vals, rows
 
 
+def gemm_algorithmic_bytes(rows_a, rows_b, kc):
+    """HBM bytes a GEMM must move: both operands once (codes 1/2 B and scales 1/32 B per element,
+    17/32 B in all) and the FP32 output once."""
+    return int((rows_a + rows_b) * kc * 17 // 32 + 4 * rows_a * rows_b)
+
+
 def measured_traffic(workload):
     """HBM bytes per GEMM launch of the step, averaged over its GEMM launches, from the committed
     FETCH_SIZE / WRITE_SIZE summary of this workload, if it was taken with the GEMM source as it
@@ -716,16 +722,22 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     kernels = {}
-    gemm_flops, gemm_s, q_bytes, q_s = 0.0, 0.0, 0.0, 0.0
+    gemm_flops, gemm_s, q_bytes, q_s, gemm_bytes = 0.0, 0.0, 0.0, 0.0, 0
     for (label, kind, spec, work), t in zip(plan.op_list, avg_ms):
         entry = {"us": round(float(t) * 1e3, 2)}
         if kind == "gemm":
             entry["tflops"] = round(work / (t * 1e-3) / 1e12, 1)
+            ra, rb = plan.out[spec[2]].shape
+            kc = int(round(work / (2.0 * ra * rb)))
+            entry["shape"] = "%dx%dx%d" % (ra, rb, kc)
+            entry["algorithmic_bytes"] = gemm_algorithmic_bytes(ra, rb, kc)
             gemm_flops += work
             gemm_s += float(t) * 1e-3
+            gemm_bytes += entry["algorithmic_bytes"]
         else:
             nbytes = work * (DUAL_BYTES_PER_ELEM if kind == "dual" else QUANT_BYTES_PER_ELEM)
             entry["gbs"] = round(nbytes / (t * 1e-3) / 1e9, 1)
+            entry["algorithmic_bytes"] = int(nbytes)
             q_bytes += nbytes
             q_s += float(t) * 1e-3
         kernels[label] = entry
@@ -736,7 +748,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MXFP4_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(args.workload),
                 "kernel": "gemm_mxfp4_pipelined (%d launches per step; achieved = GEMM FLOPs / GEMM time)" % n_gemm,
-                "algorithmic_per_launch": "2*M*N*K = %.1f GFLOP average" % (gemm_flops / n_gemm / 1e9)}
+                "algorithmic_per_launch": "2*M*N*K = %.1f GFLOP average" % (gemm_flops / n_gemm / 1e9),
+                "algorithmic_bytes_per_launch": int(gemm_bytes / n_gemm)}
     quantizer = {"gbs": round(q_bytes / q_s / 1e9, 1), "frac_of_hbm": round(q_bytes / q_s / 1e9 / HBM_PEAK_GBS, 4),
                  "bytes_per_elem": {"single": QUANT_BYTES_PER_ELEM, "dual": DUAL_BYTES_PER_ELEM},
                  "launches": "dual" if plan.dual else "separate", "us_per_step": round(q_s * 1e6, 1)}
