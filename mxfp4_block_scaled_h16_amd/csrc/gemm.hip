@@ -356,15 +356,20 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
     __shared__ __attribute__((aligned(1024))) uint8_t lds[G::kLdsBytes];
 
     // tile order: consecutive workgroups are spread over the 8 XCDs; give each XCD a contiguous
-    // range of tiles, walked column-panel by column-panel in groups of 8 row panels
+    // range of tiles, walked column-panel by column-panel in groups of row panels, so that one
+    // round of an XCD's 32 CUs covers about a square region and its operand panels are shared
+    // through that XCD's L2: 8 row panels of 256 x 256 tiles, 4 of 256 x 128 tiles (4 x 8 tiles
+    // fetch 20% fewer operand bytes per round than 8 x 4; measured 1-1.5% faster on the
+    // segmented-chain products of the decoder layer, 4.025 -> 4.006 ms per step)
     const int total = tiles_m * tiles_n;
     // split-K: workgroup blockIdx.x covers K-split blockIdx.x / total of tile blockIdx.x % total
     const int split = blockIdx.x / total;
     int t = blockIdx.x % total;
     if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;
-    const int group = 8 * tiles_n;
-    const int g0 = (t / group) * 8;
-    const int gm = min(8, tiles_m - g0);
+    constexpr int kGroupRows = 8 * TN / TM;   // a round of 32 tiles covers about a square region
+    const int group = kGroupRows * tiles_n;
+    const int g0 = (t / group) * kGroupRows;
+    const int gm = min(kGroupRows, tiles_m - g0);
     const int tm = g0 + (t % group) % gm;
     const int tn = (t % group) / gm;
     const int m0 = tm * TM, n0 = tn * TN;
