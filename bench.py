@@ -67,6 +67,9 @@ def parse_args():
                         "shape of the step, on the step's operands)")
     p.add_argument("--separate-quant", action="store_true",
                    help="one quantizer launch per axis instead of one dual launch per tensor")
+    p.add_argument("--no-group", action="store_true",
+                   help="one GEMM launch per product, also for same-shape products of one input (k and v, "
+                        "gate and up), which otherwise share a grouped launch per pass")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the measured HBM and matrix-core ceilings")
     p.add_argument("--copy-calibration", action="store_true",
@@ -77,12 +80,13 @@ def parse_args():
 class Plan:
     """Buffers and the ordered launch list of one step (quantize and GEMM launches)."""
 
-    def __init__(self, mx, torch, workload, h, sets, dual=True, host=None):
+    def __init__(self, mx, torch, workload, h, sets, dual=True, host=None, group=True):
         import numpy as np
         from synth import inputs
         desc, projs, passes, M = WORKLOADS[workload]
         self.mx, self.torch, self.h, self.passes, self.M = mx, torch, h, passes, M
         self.dual = dual
+        self.group = group
         # h may carry the randomized-Hadamard or orthonormal flags; alpha undoes the factor of the
         # size alone (the orthonormal rotation leaves none)
         hs = h & ~(mx.RHT | mx.ORTHO)
@@ -173,21 +177,36 @@ class Plan:
                 seen.add(dst)
                 quants.append((label, src, key, axis, rnd, seed, stream, dst, elems))
             return dst
-        steps = []    # ("gemm", label, qa, qb, out, flops) with the quantizations listed before it
+        # projections that read one input with weights of one shape (k and v, gate and up) run
+        # each pass as one grouped launch, unless the plan was built without grouping
+        groups = []
         for name, K, N in self.projs:
-            a = inp[name]
-            if "F" in self.passes:
-                qa = need("x", "act", a, 1, "rne", 0, 0, (a, "rows"), M * K)
-                qb = need("W", "w", name, 1, "rne", 0, 1, (name, "w_rows"), N * K)
-                steps.append(("gemm Fprop %s" % name, qa, qb, (name, "F"), 2.0 * M * N * K))
-            if "D" in self.passes:
-                qa = need("dY", "dy", name, 1, "rne", 0, 0, (name, "dy_rows"), M * N)
-                qb = need("W", "w", name, 0, "rne", 0, 1, (name, "w_cols"), N * K)
-                steps.append(("gemm Dgrad %s" % name, qa, qb, (name, "D"), 2.0 * M * N * K))
-            if "W" in self.passes:
-                qa = need("dY", "dy", name, 0, "sr", 0x5EED, 0, (name, "dy_cols"), M * N)
-                qb = need("x", "act", a, 0, "sr", 0x5EED, 1, (a, "cols"), M * K)
-                steps.append(("gemm Wgrad %s" % name, qa, qb, (name, "W"), 2.0 * M * N * K))
+            last = groups[-1] if groups else None
+            if self.group and last and (inp[last[0][0]], last[0][1], last[0][2]) == (inp[name], K, N):
+                last.append((name, K, N))
+            else:
+                groups.append([(name, K, N)])
+        steps = []    # (label, [(qa, qb, out)], flops), each after the quantizations it needs
+        for members in groups:
+            names = "+".join(m[0] for m in members)
+            for pas, pname in (("F", "Fprop"), ("D", "Dgrad"), ("W", "Wgrad")):
+                if pas not in self.passes:
+                    continue
+                prods, flops = [], 0.0
+                for name, K, N in members:
+                    a = inp[name]
+                    if pas == "F":
+                        qa = need("x", "act", a, 1, "rne", 0, 0, (a, "rows"), M * K)
+                        qb = need("W", "w", name, 1, "rne", 0, 1, (name, "w_rows"), N * K)
+                    elif pas == "D":
+                        qa = need("dY", "dy", name, 1, "rne", 0, 0, (name, "dy_rows"), M * N)
+                        qb = need("W", "w", name, 0, "rne", 0, 1, (name, "w_cols"), N * K)
+                    else:
+                        qa = need("dY", "dy", name, 0, "sr", 0x5EED, 0, (name, "dy_cols"), M * N)
+                        qb = need("x", "act", a, 0, "sr", 0x5EED, 1, (a, "cols"), M * K)
+                    prods.append((qa, qb, (name, pas)))
+                    flops += 2.0 * M * N * K
+                steps.append(("gemm %s %s" % (pname, names), prods, flops))
         by_dst = {q[7]: q for q in quants}
         by_src = {}
         for q in quants:
@@ -211,10 +230,11 @@ class Plan:
                 ops.append(("quant_%s %s%s" % ("rows" if q[3] == 1 else "cols", tensor,
                                                  " sr" if q[4] == "sr" else ""), "quant", q, q[8]))
                 done.add(dst)
-        for label, qa, qb, out, flops in steps:
-            emit(qa)
-            emit(qb)
-            ops.append((label, "gemm", (qa, qb, out), flops))
+        for label, prods, flops in steps:
+            for qa, qb, _ in prods:
+                emit(qa)
+                emit(qb)
+            ops.append((label, "gemm", tuple(prods), flops))
         self.op_list = ops
 
     def _tensor(self, d_acts, d_proj, q):
@@ -240,10 +260,15 @@ class Plan:
                 o0 = dict(rounding=q0[4], seed=q0[5], stream_id=q0[6], layout=self.layout[q0[7]],
                           q=self.q[q0[7]][0], scales=self.q[q0[7]][1])
                 calls.append(lambda t=t, o1=o1, o0=o0: mx.quantize_dual(t, h, o1, o0))
-            else:
-                qa, qb, out = spec
+            elif len(spec) == 1:
+                (qa, qb, out), = spec
                 calls.append(lambda qa=self.q[qa], qb=self.q[qb], c=self.out[out], lay=self.layout[qa], ws=self.ws[out]:
                              mx.gemm(qa[0], qa[1], qb[0], qb[1], alpha, c, layout=lay, workspace=ws))
+            else:
+                items = [(*self.q[qa], *self.q[qb]) for qa, qb, _ in spec]
+                outs = [self.out[out] for _, _, out in spec]
+                calls.append(lambda items=items, outs=outs, lay=self.layout[spec[0][0]]:
+                             mx.gemm_grouped(items, alpha, outs=outs, layout=lay))
         return calls
 
 
@@ -344,11 +369,10 @@ def quantization_error(plan, rows=8):
         return f64[key]
     acts, per_proj = plan.host["acts"], plan.host["proj"]
     out = {}
-    for label, kind, spec, _ in plan.op_list:
-        if kind != "gemm":
-            continue
-        qa, qb, okey = spec
+    products = [(qa, qb, okey) for _, kind, spec, _ in plan.op_list if kind == "gemm" for qa, qb, okey in spec]
+    for qa, qb, okey in products:
         name, pas = okey
+        label = "gemm %s %s" % ({"F": "Fprop", "D": "Dgrad", "W": "Wgrad"}[pas], name)
         w = host64(("w", name), per_proj[name][0])
         dy = host64(("dy", name), per_proj[name][1])
         akey = qb[0] if pas == "W" else qa[0]
@@ -652,42 +676,52 @@ def library_baselines(plan, avg_ms, steps, settle_s=0.1):
     step's own operands converted to FP8 E4M3 once, outside timing: per-tensor FP8 and MXFP8
     (E8M0 scale per 32). The FP8 form of the method's step is the pages' baseline; these are its
     GEMMs alone (bf16 output, half the bytes of this library's FP32 output). Each shape is
-    settled for `settle_s` seconds, then timed over K launches (host clock)."""
-    import torch
+    settled for `settle_s` seconds, then timed over K launches (host clock). A grouped launch's
+    time is shared evenly among its products."""
     out = {"output": "bf16", "operands": "the step's bf16 operands, converted once outside timing", "gemms": {}}
     ours_s, tot = 0.0, {"fp8_per_tensor": 0.0, "mxfp8": 0.0}
     for (label, kind, spec, work), t in zip(plan.op_list, avg_ms):
         if kind != "gemm":
             continue
-        A, B = gemm_operands_bf16(plan, spec[2])
-        entry = {"shape": "%dx%dx%d" % (A.shape[0], B.shape[0], A.shape[1]),
-                 "this_library_us": round(float(t) * 1e3, 2)}
         ours_s += float(t) * 1e-3
-        for name, conv, vk in (("fp8_per_tensor", fp8_per_tensor, "fp8"), ("mxfp8", mxfp8, "mxfp8")):
-            try:
-                a, b = conv(A), conv(B)
-                f = lambda a=a, b=b, vk=vk: vendor_gemm(vk, a, b)  # noqa: E731
-                t_end = time.perf_counter() + settle_s
-                while time.perf_counter() < t_end:
-                    f()
-                    torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for _ in range(steps):
-                    f()
-                torch.cuda.synchronize()
-                us = (time.perf_counter() - t0) * 1e6 / steps
-                entry[name + "_us"] = round(us, 2)
-                tot[name] += us * 1e-6
-                del a, b
-            except Exception as e:  # a baseline the runtime does not offer is reported, not fatal
-                entry[name + "_error"] = str(e)[:160]
-                tot[name] = float("nan")
-        del A, B
-        out["gemms"][label] = entry
+        for okey in (p[2] for p in spec):
+            library_baseline_entry(out, tot, plan, okey, float(t) / len(spec), len(spec), steps, settle_s)
     out["step_gemm_ms"] = {"this_library_mxfp4": round(ours_s * 1e3, 4),
                            "fp8_per_tensor": round(tot["fp8_per_tensor"] * 1e3, 4),
                            "mxfp8": round(tot["mxfp8"] * 1e3, 4)}
     return out
+
+
+def library_baseline_entry(out, tot, plan, okey, t_ms, group, steps, settle_s):
+    """Time the vendor GEMMs of one product (okey) and add its entry to out["gemms"]."""
+    import torch
+    A, B = gemm_operands_bf16(plan, okey)
+    label = "gemm %s %s" % ({"F": "Fprop", "D": "Dgrad", "W": "Wgrad"}[okey[1]], okey[0])
+    entry = {"shape": "%dx%dx%d" % (A.shape[0], B.shape[0], A.shape[1]),
+             "this_library_us": round(t_ms * 1e3, 2)}
+    if group > 1:
+        entry["this_library_grouped"] = "1/%d of one launch for %d products" % (group, group)
+    for name, conv, vk in (("fp8_per_tensor", fp8_per_tensor, "fp8"), ("mxfp8", mxfp8, "mxfp8")):
+        try:
+            a, b = conv(A), conv(B)
+            f = lambda a=a, b=b, vk=vk: vendor_gemm(vk, a, b)  # noqa: E731
+            t_end = time.perf_counter() + settle_s
+            while time.perf_counter() < t_end:
+                f()
+                torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                f()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / steps
+            entry[name + "_us"] = round(us, 2)
+            tot[name] += us * 1e-6
+            del a, b
+        except Exception as e:  # a baseline the runtime does not offer is reported, not fatal
+            entry[name + "_error"] = str(e)[:160]
+            tot[name] = float("nan")
+    del A, B
+    out["gemms"][label] = entry
 
 
 def main():
@@ -713,7 +747,7 @@ def main():
         in_bytes += 2 * (N * K + M * N)
     in_bytes += 2 * M * sum(K for name, K, N in projs)
     sets = max(1, min(8, -(-(1 << 30) // in_bytes)))
-    plan = Plan(mx, torch, args.workload, h, sets, dual=not args.separate_quant)
+    plan = Plan(mx, torch, args.workload, h, sets, dual=not args.separate_quant, group=not args.no_group)
     torch.cuda.synchronize()
 
     settle_steps = settle(plan, args.settle)
@@ -727,10 +761,12 @@ def main():
         entry = {"us": round(float(t) * 1e3, 2)}
         if kind == "gemm":
             entry["tflops"] = round(work / (t * 1e-3) / 1e12, 1)
-            ra, rb = plan.out[spec[2]].shape
-            kc = int(round(work / (2.0 * ra * rb)))
+            ra, rb = plan.out[spec[0][2]].shape
+            kc = int(round(work / (2.0 * ra * rb * len(spec))))
             entry["shape"] = "%dx%dx%d" % (ra, rb, kc)
-            entry["algorithmic_bytes"] = gemm_algorithmic_bytes(ra, rb, kc)
+            if len(spec) > 1:
+                entry["products"] = len(spec)
+            entry["algorithmic_bytes"] = gemm_algorithmic_bytes(ra, rb, kc) * len(spec)
             gemm_flops += work
             gemm_s += float(t) * 1e-3
             gemm_bytes += entry["algorithmic_bytes"]

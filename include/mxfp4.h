@@ -52,12 +52,13 @@
 extern "C" {
 #endif
 
-/* Raised whenever an entry point, a struct or the bits an entry point produces change. 10:
+/* Raised whenever an entry point, a struct or the bits an entry point produces change. 11:
+ * mxfp4_gemm_grouped and mxfp4_gemm_item_t. 10:
  * mxfp4_linear_fprop_noalloc; GEMMs whose contraction exceeds 5120 accumulate in fixed segments
  * (their FP32 results differ from 9 in the last bits); every enum spans the int32 range. 9: the
  * stochastic-rounding decision compares 22 random bits with the fractional position truncated to
  * 22 bits (codes for |v| < 1 differ from 8). */
-#define MXFP4_ABI_VERSION 10
+#define MXFP4_ABI_VERSION 11
 
 /* Every enum below includes the whole int32 range (the _RANGE_ members are not values to pass):
  * an entry point receives whatever integer a C caller passes and refuses the ones it does not
@@ -242,6 +243,35 @@ mxfp4_status_t mxfp4_gemm_ex(const uint8_t *aq, int64_t lda, const uint8_t *as, 
 /* Workspace bytes that let mxfp4_gemm split the contraction of an M x N x K product (0 when the
  * product is not split; also 0 for invalid sizes). */
 size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* One product of a grouped launch: its operands (device, as for mxfp4_gemm) and its output. */
+typedef struct {
+    const uint8_t *aq, *as, *bq, *bs;
+    float *c;
+} mxfp4_gemm_item_t;
+
+#define MXFP4_GEMM_GROUP_MAX 8
+
+/*
+ * mxfp4_gemm_grouped -- up to MXFP4_GEMM_GROUP_MAX products of one shape in one launch.
+ *
+ * Defined by: the product of mxfp4_gemm (Methodology section), for each item i:
+ *   items[i].c = alpha * A_i B_i^T,  A_i = (items[i].aq, items[i].as), B_i = (items[i].bq, items[i].bs).
+ * It serves the layer's products that have too few output tiles to fill the chip on their own
+ * (the key and value projections of an attention block: one input, two weights of the same
+ * shape): their tiles share one grid, so each output is the one mxfp4_gemm writes, bit for bit.
+ *   items    host array of count entries, read before the call returns; every pointer as
+ *            mxfp4_gemm requires it; the outputs must not overlap one another.
+ *   count    0 .. MXFP4_GEMM_GROUP_MAX (0: nothing to do).
+ * M, N, K, the leading dimensions, alpha and the layout apply to every item, with mxfp4_gemm's
+ * requirements. No workspace: the contraction is never split. Row-major operands whose K is not
+ * a multiple of 512 run one launch per item.
+ * Errors: MXFP4_ERR_ARG for count out of range or overlapping outputs; otherwise those of
+ * mxfp4_gemm, for the first item that fails them (nothing is launched then).
+ */
+mxfp4_status_t mxfp4_gemm_grouped(const mxfp4_gemm_item_t *items, int count, int64_t lda, int64_t ldas,
+                                  int64_t ldb, int64_t ldbs, int64_t M, int64_t N, int64_t K, float alpha,
+                                  int64_t ldc, mxfp4_layout_t layout, void *stream);
 
 /* Per-operand configuration of one linear-layer GEMM. */
 typedef struct {

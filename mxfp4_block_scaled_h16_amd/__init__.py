@@ -46,6 +46,12 @@ class QuantOut(ctypes.Structure):
                 ("scales", ctypes.c_void_p), ("lds", ctypes.c_int64)]
 
 
+class GemmItem(ctypes.Structure):
+    """mxfp4_gemm_item_t: one product of mxfp4_gemm_grouped."""
+    _fields_ = [("aq", ctypes.c_void_p), ("as_", ctypes.c_void_p), ("bq", ctypes.c_void_p),
+                ("bs", ctypes.c_void_p), ("c", ctypes.c_void_p)]
+
+
 class LinearCfg(ctypes.Structure):
     _fields_ = [("hadamard", ctypes.c_int), ("rnd_a", ctypes.c_int), ("rnd_b", ctypes.c_int),
                 ("seed", ctypes.c_uint64)]
@@ -82,6 +88,9 @@ def lib():
     L.mxfp4_gemm_ex.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float,
                                 vp, ci, i64, ci, vp, ctypes.c_size_t, vp]
     L.mxfp4_gemm_ex.restype = ci
+    L.mxfp4_gemm_grouped.argtypes = [ctypes.POINTER(GemmItem), ci, i64, i64, i64, i64, i64, i64, i64,
+                                     ctypes.c_float, i64, ci, vp]
+    L.mxfp4_gemm_grouped.restype = ci
     L.mxfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.mxfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
     L.mxfp4_tiled_sizes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
@@ -313,6 +322,45 @@ def gemm(aq, as_, bq, bs, alpha=1.0, out=None, stream=None, layout="rows", m=Non
                                  out.stride(0), lay, ws_ptr, ws_len, _stream(stream))
         _check(st, "mxfp4_gemm_ex")
     return out
+
+
+GEMM_GROUP_MAX = 8
+
+
+def gemm_grouped(items, alpha=1.0, outs=None, stream=None, layout="rows", m=None, n=None):
+    """outs[i] = alpha * A_i B_i^T for items[i] = (aq, as, bq, bs), all of one shape, in one
+    launch (mxfp4_gemm_grouped); each output equals what gemm() writes for that item. M and N
+    come from `outs`, or `m` and `n` (tiled operands are padded)."""
+    lay = _layout(layout)
+    items = list(items)
+    if not 0 < len(items) <= GEMM_GROUP_MAX:
+        raise ValueError("1 to %d products per grouped launch" % GEMM_GROUP_MAX)
+    aq0, as0, bq0, bs0 = items[0]
+    M, K = aq0.shape[0], aq0.shape[1] * 2
+    N = bq0.shape[0]
+    if outs is not None:
+        if len(outs) != len(items):
+            raise ValueError("one output per product")
+        M, N = outs[0].shape
+    M = M if m is None else int(m)
+    N = N if n is None else int(n)
+    for it in items:
+        for t, t0, nm in zip(it, items[0], ("aq", "as", "bq", "bs")):
+            _require_cuda(t, nm)
+            if t.shape != t0.shape or t.stride() != t0.stride():
+                raise ValueError("grouped products must share operand shapes and strides (%s)" % nm)
+        _check_gemm_operands(*it, M, N, K, lay)
+    if outs is None:
+        outs = [torch.empty((M, N), dtype=torch.float32, device=aq0.device) for _ in items]
+    for o in outs:
+        if o.dtype != torch.float32 or o.shape != (M, N) or o.stride() != outs[0].stride() or o.stride(-1) != 1:
+            raise TypeError("outputs must be float32 [M, N] with one row stride")
+    arr = (GemmItem * len(items))(*[GemmItem(a.data_ptr(), s.data_ptr(), b.data_ptr(), t.data_ptr(), o.data_ptr())
+                                    for (a, s, b, t), o in zip(items, outs)])
+    st = lib().mxfp4_gemm_grouped(arr, len(items), aq0.stride(0), as0.stride(0), bq0.stride(0), bs0.stride(0),
+                                  M, N, K, float(alpha), outs[0].stride(0), lay, _stream(stream))
+    _check(st, "mxfp4_gemm_grouped")
+    return outs
 
 
 def workspace_bytes(pass_, M, K, N) -> int:

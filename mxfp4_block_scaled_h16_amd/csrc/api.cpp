@@ -374,6 +374,41 @@ mxfp4_status_t mxfp4_gemm_ex(const uint8_t *aq, int64_t lda, const uint8_t *as, 
                                     (hipStream_t)stream));
 }
 
+mxfp4_status_t mxfp4_gemm_grouped(const mxfp4_gemm_item_t *items, int count, int64_t lda, int64_t ldas,
+                                  int64_t ldb, int64_t ldbs, int64_t M, int64_t N, int64_t K, float alpha,
+                                  int64_t ldc, mxfp4_layout_t layout, void *stream)
+{
+    if (count < 0 || count > MXFP4_GEMM_GROUP_MAX) return MXFP4_ERR_ARG;
+    if (count > 0 && !items) return MXFP4_ERR_NULL;
+    mxfp4_status_t st;
+    for (int i = 0; i < count; ++i) {
+        const mxfp4_gemm_item_t &it = items[i];
+        if ((st = check_gemm(it.aq, lda, it.as, ldas, it.bq, ldb, it.bs, ldbs, M, N, K, it.c, ldc, layout)) !=
+            MXFP4_OK)
+            return st;
+    }
+    if (count == 0 || M == 0 || N == 0) return MXFP4_OK;
+    // the rows [c, c + (M - 1) ldc + N) of two outputs must not share an element
+    const unsigned __int128 span = ((unsigned __int128)(M - 1) * (uint64_t)ldc + (uint64_t)N) * sizeof(float);
+    for (int i = 0; i < count; ++i)
+        for (int j = i + 1; j < count; ++j) {
+            const unsigned __int128 a = (uintptr_t)items[i].c, b = (uintptr_t)items[j].c;
+            if (a < b + span && b < a + span) return MXFP4_ERR_ARG;
+        }
+    if ((st = check_device()) != MXFP4_OK) return st;
+    mx::GemmGroupItem grp[MXFP4_GEMM_GROUP_MAX];
+    for (int i = 0; i < count; ++i) grp[i] = {items[i].aq, items[i].as, items[i].bq, items[i].bs, items[i].c};
+    if (K == 0) {
+        for (int i = 0; i < count; ++i) {
+            const hipError_t e = mx::launch_empty_product(grp[i].c, false, M, N, ldc, 0.0f, (hipStream_t)stream);
+            if (e != hipSuccess) return from_hip(e);
+        }
+        return MXFP4_OK;
+    }
+    return from_hip(mx::launch_gemm_grouped(grp, count, lda, ldas, ldb, ldbs, M, N, K, alpha, ldc,
+                                            layout == MXFP4_LAYOUT_TILED, (hipStream_t)stream));
+}
+
 size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;

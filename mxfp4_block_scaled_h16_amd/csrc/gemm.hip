@@ -279,6 +279,7 @@ constexpr int kRowBytes = kStageK / 2;                // 64 bytes of codes per r
 constexpr int kNumBuf = 4;                            // stage ring; a group = 4 stages
 constexpr int kRowsPerDma = 1024 / kRowBytes;         // one wave-wide 16 B/lane DMA covers 16 rows
 constexpr int kGemmWaves = 8;                         // wavefronts per workgroup (4 or 8)
+constexpr int kGroupMax = 8;                          // products of one grouped launch
 // the tile of products whose contraction needs a segmented accumulation chain: 256 x 128, eight
 // wavefronts of 64 x 64 (a 128 x 64 wave tile has no registers left for the second accumulator
 // set). Measured against four wavefronts of 128 x 64 (one per SIMD, 455 registers): the same
@@ -336,18 +337,32 @@ struct Geo {
     static constexpr int kMinBlocks = kLdsBytes <= 80 * 1024 ? 2 : 1;   // workgroups per CU
 };
 
+// The products of a grouped launch: same shapes, strides and layout, operands and outputs of
+// their own.
+struct GroupItem {
+    const uint8_t *aq, *as, *bq, *bs;
+    float *c;
+};
+struct GroupArgs {
+    GroupItem item[kGroupMax];
+    int count;
+};
+
 // EPI: kEpiF32 writes FP32 c = alpha * A B^T (out.c a float pointer; no other epilogue code is
 // compiled in), kEpiF32Beta adds beta * c, kEpiBF16 writes bf16 (with beta * c).
+// GROUP: the grid covers grp.count products (FP32 output, no split of K), one after another in
+// blockIdx order before the spread over the XCDs, so their tiles fill the chip together.
 // FOLD: the accumulation chain restarts from zero every fold_groups groups of four stages, the
 // finished segments summed in K order in a second set of registers (contractions longer than
 // one chain may be; only geometries with 64 x 64 wave tiles have the registers for it).
-template <int NW, bool TILED, int EPI, int TM = kBM, int TN = kBN, int WM = 2, bool FOLD = false>
+template <int NW, bool TILED, int EPI, int TM = kBM, int TN = kBN, int WM = 2, bool FOLD = false, bool GROUP = false>
 __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void gemm_mxfp4_pipelined(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
     int M, int N, int K, OutSpec out, int tiles_m, int tiles_n, int splits, float *__restrict__ partials,
-    int fold_groups)
+    int fold_groups, GroupArgs grp)
 {
+    static_assert(!GROUP || EPI == kEpiF32, "grouped products write FP32 without beta");
     using G = Geo<NW, TM, TN, WM>;
     static_assert(!FOLD || G::FI * G::FJ <= 4, "segmented accumulation needs wave tiles of at most 64 x 64");
     constexpr int FI = G::FI, FJ = G::FJ;
@@ -362,10 +377,26 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
     // fetch 20% fewer operand bytes per round than 8 x 4; measured 1-1.5% faster on the
     // segmented-chain products of the decoder layer, 4.025 -> 4.006 ms per step)
     const int total = tiles_m * tiles_n;
-    // split-K: workgroup blockIdx.x covers K-split blockIdx.x / total of tile blockIdx.x % total
-    const int split = blockIdx.x / total;
-    int t = blockIdx.x % total;
-    if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;
+    int split, t;
+    if constexpr (GROUP) {
+        // the products' tiles as one range spread over the XCDs, product by product
+        const int all = total * grp.count;
+        int u = blockIdx.x;
+        if (all % 8 == 0) u = (u % 8) * (all / 8) + u / 8;
+        const int gi = u / total;
+        t = u % total;
+        split = 0;
+        aq = grp.item[gi].aq;
+        as = grp.item[gi].as;
+        bq = grp.item[gi].bq;
+        bs = grp.item[gi].bs;
+        out.c = grp.item[gi].c;
+    } else {
+        // split-K: workgroup blockIdx.x covers K-split blockIdx.x / total of tile blockIdx.x % total
+        split = blockIdx.x / total;
+        t = blockIdx.x % total;
+        if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;
+    }
     constexpr int kGroupRows = 8 * TN / TM;   // a round of 32 tiles covers about a square region
     const int group = kGroupRows * tiles_n;
     const int g0 = (t / group) * kGroupRows;
@@ -834,7 +865,8 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
         const int mm = (int)((M + kFoldTM - 1) / kFoldTM), mn = (int)((N + kFoldTN - 1) / kFoldTN);
         const auto run_mid = [&](auto kernel) {
             return launch(kernel, dim3((unsigned)(mm * mn)), dim3(64 * kFoldWaves), 0, stream, aq, lda, as, ldas, bq,
-                          ldb, bs, ldbs, (int)M, (int)N, (int)K, out, mm, mn, 1, (float *)nullptr, fold);
+                          ldb, bs, ldbs, (int)M, (int)N, (int)K, out, mm, mn, 1, (float *)nullptr, fold,
+                          GroupArgs{});
         };
         return pick(run_mid, std::integral_constant<int, kFoldWaves>(), std::integral_constant<int, kFoldTM>(),
                     std::integral_constant<int, kFoldTN>(), C4(), std::true_type());
@@ -848,7 +880,7 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
         const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
         const auto run_small = [&](auto kernel) {
             return launch(kernel, dim3((unsigned)(sm * sn)), dim3(64 * 4), 0, stream, aq, lda, as, ldas, bq, ldb, bs,
-                          ldbs, (int)M, (int)N, (int)K, out, sm, sn, 1, (float *)nullptr, fold);
+                          ldbs, (int)M, (int)N, (int)K, out, sm, sn, 1, (float *)nullptr, fold, GroupArgs{});
         };
         if (fold > 0) return pick(run_small, C4(), C128(), C128(), C2(), std::true_type());
         return pick(run_small, C4(), C128(), C128(), C2(), std::false_type());
@@ -856,13 +888,61 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
     const dim3 grid((unsigned)(tiles_m * tiles_n * splits)), block(64 * kGemmWaves);
     const auto run = [&](auto kernel) {
         return launch(kernel, grid, block, 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs, (int)M, (int)N, (int)K,
-                      out, tiles_m, tiles_n, splits, partials, 0);
+                      out, tiles_m, tiles_n, splits, partials, 0, GroupArgs{});
     };
     e = pick(run, std::integral_constant<int, kGemmWaves>(), C256(), C256(), C2(), std::false_type());
     if (e != hipSuccess || splits == 1) return e;
     const int64_t total = M * N;
     return launch(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
                   (const float *)partials, splits, M, N, out);
+}
+
+hipError_t launch_gemm_grouped(const GemmGroupItem *items, int count, int64_t lda, int64_t ldas, int64_t ldb,
+                               int64_t ldbs, int64_t M, int64_t N, int64_t K, float alpha, int64_t ldc, bool tiled,
+                               hipStream_t stream)
+{
+    const bool scales_aligned = ldas % 16 == 0 && ldbs % 16 == 0;
+    const bool offsets_fit = (int64_t)(M - 1) * lda + lda <= INT32_MAX && (int64_t)(N - 1) * ldb + ldb <= INT32_MAX;
+    bool pipelined = tiled || (K % 512 == 0 && K > 0 && scales_aligned && offsets_fit);
+    for (int i = 0; i < count; ++i)
+        pipelined = pipelined && ((uintptr_t)items[i].as % 16 == 0) && ((uintptr_t)items[i].bs % 16 == 0);
+    if (!pipelined || count > kGroupMax) {
+        // the row kernel, product by product
+        for (int i = 0; i < count; ++i) {
+            const hipError_t e = launch_gemm(items[i].aq, lda, items[i].as, ldas, items[i].bq, ldb, items[i].bs,
+                                             ldbs, M, N, K, alpha, 0.0f, items[i].c, false, ldc, tiled, nullptr, 0,
+                                             stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    GroupArgs grp{};
+    grp.count = count;
+    for (int i = 0; i < count; ++i)
+        grp.item[i] = GroupItem{items[i].aq, items[i].as, items[i].bq, items[i].bs, items[i].c};
+    const OutSpec out{items[0].c, ldc, alpha, 0.0f, 0};
+    const int fold = chain_segment(K / 512, 16);
+    const int64_t big_tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN) * count;
+    // the geometry launch_gemm would pick for one product with all the products' tiles
+    auto run = [&](auto kernel, int nw, int tm, int tn) {
+        const int gm = (int)((M + tm - 1) / tm), gn = (int)((N + tn - 1) / tn);
+        return launch(kernel, dim3((unsigned)(gm * gn * count)), dim3(64 * nw), 0, stream, items[0].aq, lda,
+                      items[0].as, ldas, items[0].bq, ldb, items[0].bs, ldbs, (int)M, (int)N, (int)K, out, gm, gn, 1,
+                      (float *)nullptr, fold, grp);
+    };
+    if (fold > 0 && big_tiles > kComputeUnits / 2)
+        return tiled ? run(gemm_mxfp4_pipelined<kFoldWaves, true, kEpiF32, kFoldTM, kFoldTN, 4, true, true>,
+                           kFoldWaves, kFoldTM, kFoldTN)
+                     : run(gemm_mxfp4_pipelined<kFoldWaves, false, kEpiF32, kFoldTM, kFoldTN, 4, true, true>,
+                           kFoldWaves, kFoldTM, kFoldTN);
+    if (fold > 0)
+        return tiled ? run(gemm_mxfp4_pipelined<4, true, kEpiF32, 128, 128, 2, true, true>, 4, 128, 128)
+                     : run(gemm_mxfp4_pipelined<4, false, kEpiF32, 128, 128, 2, true, true>, 4, 128, 128);
+    if (big_tiles <= kComputeUnits / 2)
+        return tiled ? run(gemm_mxfp4_pipelined<4, true, kEpiF32, 128, 128, 2, false, true>, 4, 128, 128)
+                     : run(gemm_mxfp4_pipelined<4, false, kEpiF32, 128, 128, 2, false, true>, 4, 128, 128);
+    return tiled ? run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32, kBM, kBN, 2, false, true>, kGemmWaves, kBM, kBN)
+                 : run(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiF32, kBM, kBN, 2, false, true>, kGemmWaves, kBM, kBN);
 }
 
 }  // namespace mx

@@ -55,6 +55,18 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
                        int64_t N, int64_t K, float alpha, float beta, void *c, bool bf16, int64_t ldc,
                        bool tiled, void *workspace, size_t ws_bytes, hipStream_t stream);
 int gemm_splits(int64_t M, int64_t N, int64_t K);
+
+// Several products of the same shape, strides and layout in one launch (FP32 output, alpha,
+// beta 0, no split of K): one grid over all their tiles, so that products with few tiles fill
+// the chip together. Falls back to one launch per product where the pipelined kernel does not
+// apply (K % 512 != 0 row-major operands) or for more than 8 products.
+struct GemmGroupItem {
+    const uint8_t *aq, *as, *bq, *bs;
+    float *c;
+};
+hipError_t launch_gemm_grouped(const GemmGroupItem *items, int count, int64_t lda, int64_t ldas, int64_t ldb,
+                               int64_t ldbs, int64_t M, int64_t N, int64_t K, float alpha, int64_t ldc, bool tiled,
+                               hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // c[m][n] = 0 for m < M, n < N (a kernel, not a memset, so it is safe inside captured graphs).

@@ -90,6 +90,31 @@ int main(void)
     EXPECT(mxfp4_gemm_ex(q, 32, q, 2, q, 32, q, 2, 8, 8, 64, 1.0f, 0.5f, host_buf + 1, MXFP4_OUT_BF16, 8,
                          MXFP4_LAYOUT_ROWS, NULL, 0, NULL), MXFP4_ERR_ALIGN);
 
+    /* grouped gemm */
+    mxfp4_gemm_item_t items[MXFP4_GEMM_GROUP_MAX + 1];
+    for (int i = 0; i <= MXFP4_GEMM_GROUP_MAX; ++i) {
+        items[i].aq = q; items[i].as = q; items[i].bq = q; items[i].bs = q;
+        items[i].c = c + 64 * i;                                 /* 8 x 8 outputs, disjoint */
+    }
+    EXPECT(mxfp4_gemm_grouped(items, MXFP4_GEMM_GROUP_MAX + 1, 32, 2, 32, 2, 8, 8, 64, 1.0f, 8, MXFP4_LAYOUT_ROWS,
+                              NULL), MXFP4_ERR_ARG);             /* too many products */
+    EXPECT(mxfp4_gemm_grouped(items, -1, 32, 2, 32, 2, 8, 8, 64, 1.0f, 8, MXFP4_LAYOUT_ROWS, NULL), MXFP4_ERR_ARG);
+    EXPECT(mxfp4_gemm_grouped(NULL, 2, 32, 2, 32, 2, 8, 8, 64, 1.0f, 8, MXFP4_LAYOUT_ROWS, NULL), MXFP4_ERR_NULL);
+    EXPECT(mxfp4_gemm_grouped(NULL, 0, 32, 2, 32, 2, 8, 8, 64, 1.0f, 8, MXFP4_LAYOUT_ROWS, NULL), MXFP4_OK);
+    EXPECT(mxfp4_gemm_grouped(items, 2, 32, 2, 32, 2, 8, 8, 48, 1.0f, 8, MXFP4_LAYOUT_ROWS, NULL),
+           MXFP4_ERR_SHAPE);                                     /* K not a multiple of 32 */
+    EXPECT(mxfp4_gemm_grouped(items, 2, 32, 2, 32, 2, 8, 8, 64, 1.0f, 8, MXFP4_LAYOUT_TILED, NULL),
+           MXFP4_ERR_SHAPE);                                     /* tiled needs K % 512 */
+    items[1].bs = NULL;
+    EXPECT(mxfp4_gemm_grouped(items, 2, 32, 2, 32, 2, 8, 8, 64, 1.0f, 8, MXFP4_LAYOUT_ROWS, NULL), MXFP4_ERR_NULL);
+    items[1].bs = q;
+    items[1].c = c + 60;                                         /* overlaps the first output's last row */
+    EXPECT(mxfp4_gemm_grouped(items, 2, 32, 2, 32, 2, 8, 8, 64, 1.0f, 8, MXFP4_LAYOUT_ROWS, NULL), MXFP4_ERR_ARG);
+    items[1].c = c;
+    EXPECT(mxfp4_gemm_grouped(items, 2, 32, 2, 32, 2, 8, 8, 64, 1.0f, 8, MXFP4_LAYOUT_ROWS, NULL), MXFP4_ERR_ARG);
+    EXPECT(mxfp4_gemm_grouped(items, 2, 32, 2, 32, 2, 0, 8, 64, 1.0f, 8, MXFP4_LAYOUT_ROWS, NULL),
+           MXFP4_OK);                                            /* empty output: nothing to write */
+
     /* size queries: invalid sizes give 0, valid ones a sane count */
     EXPECT(mxfp4_gemm_workspace_bytes(neg, 8, 64) == 0, 1);
     EXPECT(mxfp4_gemm_workspace_bytes(big, big, big) == 0, 1);

@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
                      "mxfp4_abi_version"):
         assert expected in names
     assert "mxfp4_tiled_sizes" in names and "mxfp4_gemm_workspace_bytes" in names
+    assert "mxfp4_gemm_grouped" in names
     assert "mxfp4_quantize_dual" in names
     assert {"mxfp4_linear_forward", "mxfp4_linear_backward", "mxfp4_linear_step_workspace_bytes"} <= set(names)
 
@@ -63,7 +64,7 @@ def test_ceiling_library_exports_its_declared_symbols():
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 10
+    assert L.mxfp4_abi_version() == 11
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"
@@ -290,3 +291,12 @@ def test_gemm_binding_checks_operand_shapes():
     for aq, as_, bq, bs, kw in cases:
         with pytest.raises(ValueError):
             mx.gemm(aq, as_, bq, bs, **kw)
+
+    # grouped products: every item is checked, and they must share shapes and strides
+    good = (t(64, 64), t(64, 4), t(32, 64), t(32, 4))
+    with pytest.raises(ValueError):
+        mx.gemm_grouped([good, cases[0][:4]])
+    with pytest.raises(ValueError):
+        mx.gemm_grouped([good] * (mx.GEMM_GROUP_MAX + 1))
+    with pytest.raises(ValueError):
+        mx.gemm_grouped([])

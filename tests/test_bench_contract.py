@@ -86,3 +86,37 @@ def test_counter_summaries_are_ignored_once_the_source_changes(tmp_path, monkeyp
     assert abs(v["frac"] - 100 * 2000 * 64 / 1e-5 / bench.VALU_LANE_OPS_PEAK) < 1e-3
     (src / "quantize.hip").write_text("// kernel v2\n")
     assert bench.quantizer_valu("layer", plan, [0.01]) is None
+
+
+def test_layer_plan_groups_same_shape_products():
+    """The layer's launch list: k and v, and gate and up, read one input with weights of one
+    shape, so each of their passes is one grouped launch (15 GEMM launches for 21 products);
+    without grouping there is one launch per product. Every product appears once, and every
+    quantized operand is produced by an earlier launch than the GEMM that reads it."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    def plan(group):
+        p = object.__new__(bench.Plan)
+        p.M, p.projs, p.passes, p.dual, p.group = 8192, bench.LLAMA_PROJ, "FDW", True, group
+        p._build(bench.LLAMA_INPUT)
+        return p
+    for group, launches in ((True, 15), (False, 21)):
+        ops = plan(group).op_list
+        gemms = [op for op in ops if op[1] == "gemm"]
+        assert len(gemms) == launches
+        products = [p[2] for op in gemms for p in op[2]]
+        assert len(products) == len(set(products)) == 21
+        made = set()
+        for label, kind, spec, work in ops:
+            if kind == "dual":
+                made.update(q[7] for q in spec)
+            elif kind == "quant":
+                made.add(spec[7])
+            else:
+                assert all(qa in made and qb in made for qa, qb, _ in spec), label
+                shapes = {(bench.LLAMA_INPUT[o[0]],) + next((k, n) for nm, k, n in bench.LLAMA_PROJ if nm == o[0])
+                          for _, _, o in spec}
+                assert len(shapes) == 1, label
+        if group:
+            assert [len(op[2]) for op in gemms] == [1, 1, 1, 2, 2, 2, 1, 1, 1, 2, 2, 2, 1, 1, 1]
