@@ -80,10 +80,11 @@ def parse_args():
 class Plan:
     """Buffers and the ordered launch list of one step (quantize and GEMM launches)."""
 
-    def __init__(self, mx, torch, workload, h, sets, dual=True, host=None, group=True):
+    def __init__(self, mx, torch, workload, h, sets, dual=True, host=None, group=True, tokens=None):
         import numpy as np
         from synth import inputs
         desc, projs, passes, M = WORKLOADS[workload]
+        M = M if tokens is None else int(tokens)   # tests run the layer at fewer tokens
         self.mx, self.torch, self.h, self.passes, self.M = mx, torch, h, passes, M
         self.dual = dual
         self.group = group

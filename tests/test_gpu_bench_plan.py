@@ -31,11 +31,11 @@ def _oracle_operands(plan, h):
     return ops
 
 
-def _run_plan(workload, h, dual):
+def _run_plan(workload, h, dual, group=True, tokens=None):
     import bench
     import mxfp4_block_scaled_h16_amd as mx
     import torch
-    plan = bench.Plan(mx, torch, workload, h, 1, dual=dual)
+    plan = bench.Plan(mx, torch, workload, h, 1, dual=dual, group=group, tokens=tokens)
     announce("bench plan", workload, "h", h, "dual", dual, "launches", len(plan.op_list))
     for f in plan.launches(0):
         f()
@@ -47,10 +47,9 @@ def _check_outputs(plan, h, samples=None, seed=3):
     ops = _oracle_operands(plan, h)
     alpha = oracle.alpha_for(h)
     rng = np.random.default_rng(seed)
-    for label, kind, spec, work in plan.op_list:
-        if kind != "gemm":
-            continue
-        qa, qb, out = spec
+    products = [(qa, qb, out) for _, kind, spec, _ in plan.op_list if kind == "gemm" for qa, qb, out in spec]
+    for qa, qb, out in products:
+        label = "gemm %s %s" % out[::-1]
         got = host(plan.out[out])
         rows, cols = got.shape
         if samples is None:
@@ -78,13 +77,26 @@ def test_qkv_step_sampled():
     _check_outputs(plan, 16, samples=2048)
 
 
+@pytest.mark.parametrize("group", [True, False])
+def test_layer_step_sampled(group):
+    """The decoder-layer step the benchmark times, at 1024 tokens (the 7 projections' weights
+    at full size): k and v, gate and up each run as one grouped launch per pass (or one launch per
+    product), dual quantizers with SR on the Wgrad operands. 1024 sampled outputs per product
+    plus the corners, against the oracle."""
+    plan = _run_plan("layer", 16, True, group=group, tokens=1024)
+    n_launch = sum(1 for _, kind, _, _ in plan.op_list if kind == "gemm")
+    assert n_launch == (15 if group else 21)
+    _check_outputs(plan, 16, samples=1024)
+
+
 def test_quantization_error_report():
     """The benchmark's method-error figure on the small workload: every GEMM is reported, and
     each relative error is that of MXFP4 (a few to a few tens of percent), neither 0 nor 1."""
     import bench
     plan = _run_plan("small", 16, True)
     err = bench.quantization_error(plan, rows=8)
-    labels = [label for label, kind, _, _ in plan.op_list if kind == "gemm"]
+    labels = ["gemm %s %s" % ({"F": "Fprop", "D": "Dgrad", "W": "Wgrad"}[o[1]], o[0])
+              for _, kind, spec, _ in plan.op_list if kind == "gemm" for _, _, o in spec]
     assert set(labels) <= set(err)
     for label in labels:
         assert 0.005 < err[label] < 0.35, (label, err[label])
