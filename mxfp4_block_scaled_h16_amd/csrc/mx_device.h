@@ -225,6 +225,52 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return r;
 }
 
+// NB consecutive Philox4x32-10 blocks, counters (c + b, c >> 32, stream_id, 0) for b < NB, with
+// c a multiple of NB (so c + b never carries into counter word 1). Counter words 1-3 are the same
+// for every block, and so are two of the first rounds' products: round 1 multiplies word 2 (the
+// stream) and round 2 multiplies word 0 (which round 1 made from words 1 and 2 and the key only).
+// Those two 64-bit multiply-adds are formed once, leaving 18 of 20 per block. COMPLEMENT as for
+// philox4x32_10.
+template <int NB, bool COMPLEMENT>
+__device__ __forceinline__ void philox4x32_10_run(uint64_t c, uint32_t stream_id, uint32_t k0, uint32_t k1,
+                                                  Philox4 (&out)[NB])
+{
+    const uint32_t c_lo = (uint32_t)c, c_hi = (uint32_t)(c >> 32);
+    // round 1, shared part: word 2's product; the new words 0 and 1
+    const uint64_t q1 = (uint64_t)0xCD9E8D57u * stream_id;
+    const uint32_t w0_1 = __builtin_amdgcn_bitop3_b32((uint32_t)(q1 >> 32), c_hi, k0, 0x96);
+    const uint32_t w1_1 = (uint32_t)q1;
+    // round 2, shared part: word 0's product
+    const uint32_t k0_2 = k0 + 0x9E3779B9u, k1_2 = k1 + 0xBB67AE85u;
+    const uint64_t p2 = (uint64_t)0xD2511F53u * w0_1;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        // round 1, per block: word 0's product (word 3 of the counter is 0)
+        const uint64_t p1 = (uint64_t)0xD2511F53u * (c_lo + (uint32_t)b);
+        const uint32_t w2_1 = (uint32_t)(p1 >> 32) ^ k1;
+        const uint32_t w3_1 = (uint32_t)p1;
+        // round 2, per block: word 2's product
+        const uint64_t q2 = (uint64_t)0xCD9E8D57u * w2_1;
+        uint32_t x0 = __builtin_amdgcn_bitop3_b32((uint32_t)(q2 >> 32), w1_1, k0_2, 0x96);
+        uint32_t x2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p2 >> 32), w3_1, k1_2, 0x96);
+        uint32_t x1 = (uint32_t)q2;
+        uint32_t x3 = (uint32_t)p2;
+        // rounds 3-10
+        uint32_t kk0 = k0_2 + 0x9E3779B9u, kk1 = k1_2 + 0xBB67AE85u;
+#pragma unroll
+        for (int round = 2; round < 9; ++round) {
+            philox_round<0x96>(x0, x1, x2, x3, kk0, kk1);
+            kk0 += 0x9E3779B9u;
+            kk1 += 0xBB67AE85u;
+        }
+        philox_round<COMPLEMENT ? 0x69 : 0x96>(x0, x1, x2, x3, kk0, kk1);
+        out[b].w[0] = x0;
+        out[b].w[1] = COMPLEMENT ? ~x1 : x1;
+        out[b].w[2] = x2;
+        out[b].w[3] = COMPLEMENT ? ~x3 : x3;
+    }
+}
+
 // ---------------------------------------------------------------- randomized Hadamard -------
 // Sign diagonal of the randomized rotation y = H (d .* x): bit t of the returned word is set iff
 // position 32 c + t along the quantized axis is negated. Word c % 4 of the Philox4x32-10 block
@@ -249,8 +295,8 @@ __device__ __forceinline__ void apply_signs(float *v, uint32_t bits)
 // ---------------------------------------------------------------------------- stochastic -----
 // Stochastic codes of 8 consecutive values y[0..7] (block scale byte S, values already
 // pre-doubled when S = 0, divisor = e8m0_divisor(S)) whose first element has position index0 (a
-// multiple of 8) in the quantized output: word k of Philox block (index0 / 4 + b) for element
-// 4 b + k.
+// multiple of 8) in the quantized output: element 4 b + k draws word k of Philox block
+// (index0 / 4 + b).
 //
 // gfx950's v_cvt_scalef32_sr_pk_fp4_f32 divides a pair of binary32 values by the scale and
 // rounds each to E2M1 stochastically, saturating at 6 and keeping the sign of the value (also
@@ -271,14 +317,10 @@ __device__ __forceinline__ uint32_t sr_fp4_byte0(float y, uint32_t nr, float div
     return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, nr, divisor, 0);
 }
 
-__device__ __forceinline__ uint32_t encode8_stochastic(const float *y, float divisor, uint64_t index0,
-                                                       uint32_t key0, uint32_t key1, uint32_t stream_id)
+// The same from the complemented words (~r) of the two blocks, r0 for elements 0-3 and r1 for 4-7.
+__device__ __forceinline__ uint32_t encode8_sr_words(const float *y, float divisor, const Philox4 &r0,
+                                                     const Philox4 &r1)
 {
-    const uint64_t c = index0 >> 2;
-    // complemented words (~r), as the conversion takes them
-    const Philox4 r0 = philox4x32_10<true>((uint32_t)c, (uint32_t)(c >> 32), stream_id, 0u, key0, key1);
-    const uint64_t c1 = c + 1;
-    const Philox4 r1 = philox4x32_10<true>((uint32_t)c1, (uint32_t)(c1 >> 32), stream_id, 0u, key0, key1);
     // byte 0 of p_k = codes of elements 2k (low nibble) and 2k + 1 (high nibble)
     const uint32_t p0 = (sr_fp4_byte0(y[1], r0.w[1], divisor) << 4) | sr_fp4_byte0(y[0], r0.w[0], divisor);
     const uint32_t p1 = (sr_fp4_byte0(y[3], r0.w[3], divisor) << 4) | sr_fp4_byte0(y[2], r0.w[2], divisor);
@@ -288,6 +330,18 @@ __device__ __forceinline__ uint32_t encode8_stochastic(const float *y, float div
     const uint32_t q01 = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);  // [p0.b0, p1.b0, 0, 0]
     const uint32_t q23 = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);  // [0, 0, p2.b0, p3.b0]
     return q01 | q23;
+}
+
+// Stochastic codes of W * 8 consecutive values (index0 a multiple of 4 W): word w of the result
+// holds values 8 w .. 8 w + 7, from the 2 W Philox blocks formed as one run.
+template <int W>
+__device__ __forceinline__ void encode_stochastic(const float *y, float divisor, uint64_t index0, uint32_t key0,
+                                                  uint32_t key1, uint32_t stream_id, uint32_t (&words)[W])
+{
+    Philox4 r[2 * W];
+    philox4x32_10_run<2 * W, true>(index0 >> 2, stream_id, key0, key1, r);
+#pragma unroll
+    for (int w = 0; w < W; ++w) words[w] = encode8_sr_words(y + 8 * w, divisor, r[2 * w], r[2 * w + 1]);
 }
 
 // ---------------------------------------------------------------------------- cross-lane ------

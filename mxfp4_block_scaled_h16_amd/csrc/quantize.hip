@@ -181,8 +181,10 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
         const float div = e8m0_divisor(sc);
         if constexpr (SR) {
             const uint64_t index0 = (uint64_t)row[u] * (uint64_t)L + (uint64_t)grp[u] * 16u;
-            w0 = encode8_stochastic(v[u], div, index0, key0, key1, stream_id);
-            w1 = encode8_stochastic(v[u] + 8, div, index0 + 8u, key0, key1, stream_id);
+            uint32_t w[2];
+            encode_stochastic<2>(v[u], div, index0, key0, key1, stream_id, w);
+            w0 = w[0];
+            w1 = w[1];
         } else {
             w0 = encode8_nearest(v[u], div);
             w1 = encode8_nearest(v[u] + 8, div);
@@ -298,9 +300,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
                 const float div = e8m0_divisor(sc);
                 if constexpr (SR) {
                     const uint64_t index0 = (uint64_t)(c0 + tc) * (uint64_t)rows + (uint64_t)(r0 + 32 * blk);
-#pragma unroll
-                    for (int wd = 0; wd < 4; ++wd)
-                        words[wd] = encode8_stochastic(v[cc] + 8 * wd, div, index0 + 8 * wd, key0, key1, stream_id);
+                    encode_stochastic<4>(v[cc], div, index0, key0, key1, stream_id, words);
                 } else {
 #pragma unroll
                     for (int wd = 0; wd < 4; ++wd) words[wd] = encode8_nearest(v[cc] + 8 * wd, div);
@@ -474,8 +474,10 @@ __global__ __launch_bounds__(64 * NW) void quant_dual_kernel(
             const float div = e8m0_divisor(sc);
             if (o1.sr) {
                 const uint64_t index0 = (uint64_t)o * cols + 16u * g;
-                w0 = encode8_stochastic(v, div, index0, o1.key0, o1.key1, o1.stream_id);
-                w1 = encode8_stochastic(v + 8, div, index0 + 8u, o1.key0, o1.key1, o1.stream_id);
+                uint32_t w[2];
+                encode_stochastic<2>(v, div, index0, o1.key0, o1.key1, o1.stream_id, w);
+                w0 = w[0];
+                w1 = w[1];
             } else {
                 w0 = encode8_nearest(v, div);
                 w1 = encode8_nearest(v + 8, div);
@@ -539,9 +541,7 @@ __global__ __launch_bounds__(64 * NW) void quant_dual_kernel(
             const float div = e8m0_divisor(sc);
             if (o0.sr) {
                 const uint64_t index0 = (uint64_t)(c0 + tc) * rows + r0 + 32 * blk;
-#pragma unroll
-                for (int wd = 0; wd < 4; ++wd)
-                    words[wd] = encode8_stochastic(v[cc] + 8 * wd, div, index0 + 8 * wd, o0.key0, o0.key1, o0.stream_id);
+                encode_stochastic<4>(v[cc], div, index0, o0.key0, o0.key1, o0.stream_id, words);
             } else {
 #pragma unroll
                 for (int wd = 0; wd < 4; ++wd) words[wd] = encode8_nearest(v[cc] + 8 * wd, div);
