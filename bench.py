@@ -317,16 +317,19 @@ def measured_traffic(workload):
         return None
 
 
-VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9   # CUs x SIMDs x lanes x clock: 39.3 T lane-ops/s
+# CUs x SIMDs x lanes per clock x clock: 78.6 T lane-ops/s. A SIMD issues a 32-bit wave64 VALU
+# instruction every two clocks (the published 157.3 TFLOP/s FP32 vector rate counts an FMA as two
+# operations; a probe of dependent-free adds measured 2.2 clocks per wave64 instruction).
+VALU_LANE_OPS_PEAK = 256 * 4 * 32 * 2.4e9
 
 
 def quantizer_valu(workload, plan, avg_ms):
     """The stochastic-rounding quantizer launches against the VALU roofline: VALU instructions
     per wavefront and wavefronts per launch from the committed SQ counter summary of this
     workload (taken with the quantizer source as it is now, else None), times 64 lanes, over the
-    launch's duration in this run, against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz. Counts every
-    VALU instruction as one issue per 16 lanes (the 64-bit multiply-adds of Philox take longer,
-    so the VALU is busier than this says)."""
+    launch's duration in this run, against 256 CUs x 4 SIMDs x 32 lanes per clock x 2.4 GHz.
+    Counts every VALU instruction as one issue slot; the 64-bit multiply-adds of Philox take
+    about 2.8 slots each (measured), so the VALU is busier than this says."""
     got = _profile_values("quant_%s_step_sq_counters.txt" % workload, "quantize.hip")
     if got is None:
         return None
