@@ -67,6 +67,9 @@ def parse_args():
                         "shape of the step, on the step's operands)")
     p.add_argument("--separate-quant", action="store_true",
                    help="one quantizer launch per axis instead of one dual launch per tensor")
+    p.add_argument("--no-graph", action="store_true",
+                   help="launch every kernel of the timed steps from the host instead of replaying each step "
+                        "as one captured HIP graph")
     p.add_argument("--no-group", action="store_true",
                    help="one GEMM launch per product, also for same-shape products of one input (k and v, "
                         "gate and up), which otherwise share a grouped launch per pass")
@@ -493,39 +496,82 @@ class TimingEvents:
         self.events = []
 
 
-def settle(plan, seconds):
+def capture_steps(plan):
+    """One HIP graph per input set (torch.cuda.CUDAGraph), each holding every launch of one step
+    on that set, after one eager run of the step on a side stream. The library launches only
+    kernels (no memset, copy or allocation) on the stream it is given: the capture stream here."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for i in range(len(plan.sets)):
+            for f in plan.launches(i):
+                f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(len(plan.sets)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in plan.launches(i):
+                f()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def step_runner(plan, graphs):
+    """f(step index) that runs one step: a graph replay, or the eager launches."""
+    if graphs:
+        return lambda s: graphs[s % len(graphs)].replay()
+
+    def eager(s):
+        for f in plan.launches(s):
+            f()
+    return eager
+
+
+def settle(plan, seconds, graphs=None):
     """Untimed steps until `seconds` of wall time have passed: the GPU leaves its idle clock
     state only after some tens of milliseconds of sustained load (a cold start measured 10-15%
     slower than the steady state of a training loop). Returns the number of steps run."""
     import torch
+    run = step_runner(plan, graphs)
     n, t_end = 0, time.perf_counter() + seconds
     while time.perf_counter() < t_end:
-        for f in plan.launches(n):
-            f()
+        run(n)
         n += 1
         torch.cuda.synchronize()
     return n
 
 
-def run_timed(plan, steps, warmup):
+def run_timed(plan, steps, warmup, graphs=None):
     """W untimed warm-up steps, then EXACTLY K timed steps bracketed by device synchronizations
-    (host clock, no per-launch instrumentation), then K more steps with fence-free HIP events
+    (host clock, no per-launch instrumentation; each step one graph replay when `graphs` holds
+    the captured steps), then K more steps launched from the host with fence-free HIP events
     around every launch on the launch stream for the per-kernel durations.
     Returns (ms per step of the timed steps, average ms of each launch of the step, ms of each
     instrumented step from its first launch's start to its last launch's end)."""
     import numpy as np
     import torch
+    run = step_runner(plan, graphs)
     for s in range(warmup):
-        for f in plan.launches(s):
-            f()
+        run(s)
     calls = [plan.launches(s) for s in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        for f in calls[s]:
-            f()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if graphs:
+        t0 = time.perf_counter()
+        for s in range(steps):
+            graphs[s % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        t0 = time.perf_counter()
+        for s in range(steps):
+            for f in calls[s]:
+                f()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ev = TimingEvents()
     stream = torch.cuda.current_stream().cuda_stream
     n_launch = len(plan.op_list)
@@ -753,9 +799,10 @@ def main():
     sets = max(1, min(8, -(-(1 << 30) // in_bytes)))
     plan = Plan(mx, torch, args.workload, h, sets, dual=not args.separate_quant, group=not args.no_group)
     torch.cuda.synchronize()
+    graphs = None if args.no_graph else capture_steps(plan)
 
-    settle_steps = settle(plan, args.settle)
-    ms_per_step, avg_ms, step_ms = run_timed(plan, args.steps, args.warmup)
+    settle_steps = settle(plan, args.settle, graphs)
+    ms_per_step, avg_ms, step_ms = run_timed(plan, args.steps, args.warmup, graphs)
     step_flops = sum(w for _, kind, _, w in plan.op_list if kind == "gemm")
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -846,8 +893,12 @@ def main():
                    "M": M, "hadamard": hsize, "randomized_hadamard": bool(args.rht), "passes": passes,
                    "input_sets": sets},
         "timing": {"settle_s": args.settle, "settle_steps": settle_steps,
-                   "value": "host clock over the K timed steps, no per-launch instrumentation",
-                   "kernels": "a second pass of K steps with fence-free HIP events around every launch",
+                   "value": ("host clock over the K timed steps, each one replay of the step captured as one HIP "
+                             "graph, no per-launch instrumentation" if graphs else
+                             "host clock over the K timed steps launched from the host, no per-launch "
+                             "instrumentation"),
+                   "kernels": "a second pass of K steps launched from the host with fence-free HIP events around "
+                              "every launch",
                    "instrumented_step_ms": {"median": round(float(np.median(step_ms)), 4),
                                             "min": round(float(step_ms.min()), 4),
                                             "max": round(float(step_ms.max()), 4)}},
