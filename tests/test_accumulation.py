@@ -68,10 +68,12 @@ def test_adversarial_operands_reach_the_worst_case():
         assert (abs(float(chain) - ref[0, 0]) <= 1e-5 * basis[0, 0]) == ok
 
 
-# (M, N, K) pick the launch: 4096 x 2304 has 144 output tiles of 256 x 256, 2048 x 2048 has 64
-# (128 x 128 tiles), 256 x 256 splits K over workgroups -- unless a split's chain would itself be
-# too long (K = 131072)
-CASES = [(4096, 2304, 6144), (4096, 2304, 8192), (4096, 2304, 14336), (4096, 2304, 28672),
+# (M, N, K) pick the launch: 4096 x 2304 has 144 output tiles of 256 x 256 (segmented chains on
+# 256 x 128 tiles; K = 10240 and 10752 put the segment boundaries at different groups), 2048 x
+# 2048 has 64 (128 x 128 tiles), 256 x 256 splits K over workgroups -- unless a split's chain
+# would itself be too long (K = 131072)
+CASES = [(4096, 2304, 6144), (4096, 2304, 8192), (4096, 2304, 10240), (4096, 2304, 10752),
+         (4096, 2304, 14336), (4096, 2304, 28672),
          (2048, 2048, 8192), (2048, 2048, 28672),
          (256, 256, 8192), (256, 256, 28672), (256, 256, 131072)]
 

@@ -387,3 +387,30 @@ def test_gemm_rows_layout_large_tiles():
     ns = np.concatenate([rng.integers(0, N, 4096), np.tile(edge_n, len(edge_m))])
     ref, basis = oracle.gemm_sampled(aq, as_, bq, bs, ms, ns, alpha=0.5)
     assert_gemm_close(got[ms, ns], ref, basis, TOL, "rows layout, large tiles")
+
+
+@pytest.mark.parametrize("M,N,K,layout", [(2300, 3900, 8192, "rows"), (2300, 3900, 6144, "tiled"),
+                                          (2300, 3900, 10240, "tiled"), (2300, 3900, 10752, "rows")])
+def test_gemm_long_contraction_ragged_tiles(M, N, K, layout):
+    """Contractions beyond 5120 on more than 128 tiles of 256 x 256 (here 9 x 16, ragged last row
+    and column): the segmented chains on 256 x 128 tiles, with segment boundaries at different
+    groups of four stages (6144: 2 x 6 groups; 8192: 2 x 8; 10240: 2 x 10; 10752: 3 x 7). 4096
+    sampled outputs plus the ragged corners against the oracle."""
+    from tests.gpu_util import tile
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(M + N + K)
+    aq, as_ = random_operand(rng, M, K)
+    bq, bs = random_operand(rng, N, K)
+    if layout == "tiled":
+        da = [_dev_u8(t.reshape(-(-M // 256) * 256, -1)) for t in tile(aq, as_, M, K)]
+        db = [_dev_u8(t.reshape(-(-N // 256) * 256, -1)) for t in tile(bq, bs, N, K)]
+    else:
+        da, db = [_dev_u8(aq), _dev_u8(as_)], [_dev_u8(bq), _dev_u8(bs)]
+    announce("gemm long K ragged", M, N, K, layout)
+    c = host(mx.gemm(*da, *db, alpha=0.0625, layout=layout, m=M, n=N))
+    edge_m = [0, 127, 128, 255, 256, 2047, 2048, 2175, 2176, M - 1]
+    edge_n = [0, 63, 64, 127, 128, 3839, 3840, 3871, 3872, N - 1]
+    ms = np.concatenate([rng.integers(0, M, 4096), np.repeat(edge_m, len(edge_n))])
+    ns = np.concatenate([rng.integers(0, N, 4096), np.tile(edge_n, len(edge_m))])
+    ref, basis = oracle.gemm_sampled(aq, as_, bq, bs, ms, ns, alpha=0.0625)
+    assert_gemm_close(c[ms, ns], ref, basis, TOL, "long K ragged %dx%dx%d %s" % (M, N, K, layout))
