@@ -72,7 +72,8 @@ def parse_args():
                         "as one captured HIP graph")
     p.add_argument("--no-group", action="store_true",
                    help="one GEMM launch per product, also for same-shape products of one input (k and v, "
-                        "gate and up), which otherwise share a grouped launch per pass")
+                        "gate and up), which otherwise share a grouped launch per pass; and one quantizer "
+                        "launch per tensor, where back-to-back dual quantizations otherwise share one")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the measured HBM and matrix-core ceilings")
     p.add_argument("--copy-calibration", action="store_true",
@@ -226,7 +227,7 @@ class Plan:
                 q1 = next(t for t in both if t[3] == 1)
                 q0 = next(t for t in both if t[3] == 0)
                 tensor = q[2] if q[1] == "act" else "%s_%s" % (q[0], q[2])
-                ops.append(("quant_dual %s" % tensor, "dual", (q1, q0), q[8]))
+                ops.append(("quant_dual %s" % tensor, "dual", ((q1, q0),), q[8]))
                 done.add(q1[7])
                 done.add(q0[7])
             else:
@@ -239,6 +240,18 @@ class Plan:
                 emit(qa)
                 emit(qb)
             ops.append((label, "gemm", tuple(prods), flops))
+        if self.group:
+            # dual quantizations that run back to back (an activation and the weight of the
+            # product that reads it, k and v, gate and up) share one launch
+            merged = []
+            for op in ops:
+                last = merged[-1] if merged else None
+                if op[1] == "dual" and last is not None and last[1] == "dual" and len(last[2]) + len(op[2]) <= 8:
+                    merged[-1] = (last[0] + "+" + op[0][len("quant_dual "):], "dual", last[2] + op[2],
+                                  last[3] + op[3])
+                else:
+                    merged.append(op)
+            ops = merged
         self.op_list = ops
 
     def _tensor(self, d_acts, d_proj, q):
@@ -257,13 +270,18 @@ class Plan:
                 calls.append(lambda t=t, axis=axis, rnd=rnd, seed=seed, stream=stream, q=q, s=s, lay=self.layout[dst]:
                              mx.quantize(t, axis, h, rnd, seed, stream, q, s, layout=lay))
             elif kind == "dual":
-                q1, q0 = spec
-                t = self._tensor(d_acts, d_proj, q1)
-                o1 = dict(rounding=q1[4], seed=q1[5], stream_id=q1[6], layout=self.layout[q1[7]],
-                          q=self.q[q1[7]][0], scales=self.q[q1[7]][1])
-                o0 = dict(rounding=q0[4], seed=q0[5], stream_id=q0[6], layout=self.layout[q0[7]],
-                          q=self.q[q0[7]][0], scales=self.q[q0[7]][1])
-                calls.append(lambda t=t, o1=o1, o0=o0: mx.quantize_dual(t, h, o1, o0))
+                items = []
+                for q1, q0 in spec:
+                    t = self._tensor(d_acts, d_proj, q1)
+                    o1 = dict(rounding=q1[4], seed=q1[5], stream_id=q1[6], layout=self.layout[q1[7]],
+                              q=self.q[q1[7]][0], scales=self.q[q1[7]][1])
+                    o0 = dict(rounding=q0[4], seed=q0[5], stream_id=q0[6], layout=self.layout[q0[7]],
+                              q=self.q[q0[7]][0], scales=self.q[q0[7]][1])
+                    items.append((t, o1, o0))
+                if len(items) == 1:
+                    calls.append(lambda it=items[0]: mx.quantize_dual(it[0], h, it[1], it[2]))
+                else:
+                    calls.append(lambda items=items: mx.quantize_dual_grouped(items, h))
             elif len(spec) == 1:
                 (qa, qb, out), = spec
                 calls.append(lambda qa=self.q[qa], qb=self.q[qb], c=self.out[out], lay=self.layout[qa], ws=self.ws[out]:
@@ -347,7 +365,7 @@ def quantizer_valu(workload, plan, avg_ms):
     for (label, kind, spec, _), t in zip(plan.op_list, avg_ms):
         if kind != "dual" or label not in counts:
             continue
-        if not any(q[4] == "sr" for q in spec):
+        if not any(q[4] == "sr" for pair in spec for q in pair):
             continue
         waves, per_wave = counts[label]
         ops = waves * per_wave * 64
@@ -426,7 +444,7 @@ def cpu_baseline(plan, h):
     rate_cols = w0.size / (time.perf_counter() - t0)
     t_quant = 0.0
     for label, kind, spec, work in plan.op_list:
-        for q in (spec if kind == "dual" else (spec,) if kind == "quant" else ()):
+        for q in ([x for pair in spec for x in pair] if kind == "dual" else (spec,) if kind == "quant" else ()):
             axis, rnd = q[3], q[4]
             rate = rate_rows if axis == 1 else (rate_cols_sr if rnd == "sr" else rate_cols)
             t_quant += work / rate

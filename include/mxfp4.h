@@ -52,13 +52,14 @@
 extern "C" {
 #endif
 
-/* Raised whenever an entry point, a struct or the bits an entry point produces change. 11:
- * mxfp4_gemm_grouped and mxfp4_gemm_item_t. 10:
+/* Raised whenever an entry point, a struct or the bits an entry point produces change. 12:
+ * mxfp4_quantize_dual_grouped and mxfp4_dual_item_t. 11: mxfp4_gemm_grouped and
+ * mxfp4_gemm_item_t. 10:
  * mxfp4_linear_fprop_noalloc; GEMMs whose contraction exceeds 5120 accumulate in fixed segments
  * (their FP32 results differ from 9 in the last bits); every enum spans the int32 range. 9: the
  * stochastic-rounding decision compares 22 random bits with the fractional position truncated to
  * 22 bits (codes for |v| < 1 differ from 8). */
-#define MXFP4_ABI_VERSION 11
+#define MXFP4_ABI_VERSION 12
 
 /* Every enum below includes the whole int32 range (the _RANGE_ members are not values to pass):
  * an entry point receives whatever integer a C caller passes and refuses the ones it does not
@@ -194,6 +195,34 @@ typedef struct {
 mxfp4_status_t mxfp4_quantize_dual(const void *x, mxfp4_dtype_t dtype, int64_t rows, int64_t cols,
                                    int64_t ldx, int hadamard, const mxfp4_quant_out_t *out_axis1,
                                    const mxfp4_quant_out_t *out_axis0, void *stream);
+
+/* One tensor of mxfp4_quantize_dual_grouped: the arguments mxfp4_quantize_dual takes for it. */
+typedef struct {
+    const void *x;
+    mxfp4_dtype_t dtype;
+    int64_t rows, cols, ldx;
+    mxfp4_quant_out_t axis1, axis0;
+} mxfp4_dual_item_t;
+
+#define MXFP4_DUAL_GROUP_MAX 8
+
+/*
+ * mxfp4_quantize_dual_grouped -- the dual quantizations of up to MXFP4_DUAL_GROUP_MAX tensors
+ * in one launch.
+ *
+ * Defined by: mxfp4_quantize_dual (Methodology section), for each item; the outputs are bitwise
+ * those of the separate calls. It serves the operands a training step quantizes back to back
+ * (an activation and the weight of the product that reads it, the key and value weights), so
+ * that small tensors share one grid instead of each leaving most of the chip idle.
+ *   items    host array of count entries, read before the call returns; each as
+ *            mxfp4_quantize_dual requires it; every item has the same dtype; no output may
+ *            overlap another output or any input.
+ *   count    0 .. MXFP4_DUAL_GROUP_MAX (0: nothing to do).
+ * Errors: MXFP4_ERR_ARG for count out of range or mixed dtypes; otherwise those of
+ * mxfp4_quantize_dual, for the first item that fails them (nothing is launched then).
+ */
+mxfp4_status_t mxfp4_quantize_dual_grouped(const mxfp4_dual_item_t *items, int count, int hadamard,
+                                           void *stream);
 
 /*
  * mxfp4_gemm -- block-scaled FP4 GEMM with FP32 accumulation and output.

@@ -46,6 +46,12 @@ class QuantOut(ctypes.Structure):
                 ("scales", ctypes.c_void_p), ("lds", ctypes.c_int64)]
 
 
+class DualItem(ctypes.Structure):
+    """mxfp4_dual_item_t: one tensor of mxfp4_quantize_dual_grouped."""
+    _fields_ = [("x", ctypes.c_void_p), ("dtype", ctypes.c_int), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ldx", ctypes.c_int64), ("axis1", QuantOut), ("axis0", QuantOut)]
+
+
 class GemmItem(ctypes.Structure):
     """mxfp4_gemm_item_t: one product of mxfp4_gemm_grouped."""
     _fields_ = [("aq", ctypes.c_void_p), ("as_", ctypes.c_void_p), ("bq", ctypes.c_void_p),
@@ -88,6 +94,8 @@ def lib():
     L.mxfp4_gemm_ex.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float,
                                 vp, ci, i64, ci, vp, ctypes.c_size_t, vp]
     L.mxfp4_gemm_ex.restype = ci
+    L.mxfp4_quantize_dual_grouped.argtypes = [ctypes.POINTER(DualItem), ci, ci, vp]
+    L.mxfp4_quantize_dual_grouped.restype = ci
     L.mxfp4_gemm_grouped.argtypes = [ctypes.POINTER(GemmItem), ci, i64, i64, i64, i64, i64, i64, i64,
                                      ctypes.c_float, i64, ci, vp]
     L.mxfp4_gemm_grouped.restype = ci
@@ -242,6 +250,33 @@ def quantize_dual(x, hadamard=16, axis1=None, axis0=None, stream=None):
                                    ctypes.byref(o1), ctypes.byref(o0), _stream(stream))
     _check(st, "mxfp4_quantize_dual")
     return q1, s1, q0, s0
+
+
+DUAL_GROUP_MAX = 8
+
+
+def quantize_dual_grouped(items, hadamard=16, stream=None):
+    """quantize_dual of several tensors in one launch: items is a list of (x, axis1, axis0) with
+    the meanings quantize_dual gives them (all x of one dtype, at most DUAL_GROUP_MAX). Returns
+    [(q1, s1, q0, s0)] per item, bit-identical to quantize_dual of each."""
+    items = list(items)
+    if not 0 < len(items) <= DUAL_GROUP_MAX:
+        raise ValueError("1 to %d tensors per grouped launch" % DUAL_GROUP_MAX)
+    outs, arr = [], (DualItem * len(items))()
+    for i, (x, axis1, axis0) in enumerate(items):
+        _require_cuda(x, "x")
+        if x.dim() != 2 or x.stride(1) != 1:
+            raise ValueError("x must be 2-D with unit column stride")
+        dtype = {torch.bfloat16: BF16, torch.float32: F32}.get(x.dtype)
+        if dtype is None:
+            raise TypeError("x must be bfloat16 or float32")
+        q1, s1, o1 = _dual_out(x, axis1, 1)
+        q0, s0, o0 = _dual_out(x, axis0, 0)
+        arr[i] = DualItem(x.data_ptr(), dtype, x.shape[0], x.shape[1], x.stride(0), o1, o0)
+        outs.append((q1, s1, q0, s0))
+    st = lib().mxfp4_quantize_dual_grouped(arr, len(items), hadamard, _stream(stream))
+    _check(st, "mxfp4_quantize_dual_grouped")
+    return outs
 
 
 def _check_gemm_operands(aq, as_, bq, bs, M, N, K, lay):

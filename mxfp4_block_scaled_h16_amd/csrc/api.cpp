@@ -340,6 +340,42 @@ mxfp4_status_t mxfp4_quantize_dual(const void *x, mxfp4_dtype_t dtype, int64_t r
                                              conv(b), (hipStream_t)stream));
 }
 
+static_assert(MXFP4_DUAL_GROUP_MAX == mx::kDualGroupMax, "grouped dual quantizer capacity");
+
+mxfp4_status_t mxfp4_quantize_dual_grouped(const mxfp4_dual_item_t *items, int count, int hadamard,
+                                           void *stream)
+{
+    if (count < 0 || count > MXFP4_DUAL_GROUP_MAX) return MXFP4_ERR_ARG;
+    if (count == 0) return MXFP4_OK;
+    if (!items) return MXFP4_ERR_NULL;
+    mxfp4_status_t st;
+    bool any = false;
+    for (int i = 0; i < count; ++i) {
+        const mxfp4_dual_item_t &it = items[i];
+        if (it.dtype != items[0].dtype) return MXFP4_ERR_ARG;
+        const mxfp4_quant_out_t &a = it.axis1, &b = it.axis0;
+        if ((st = check_quantize(it.x, it.dtype, it.rows, it.cols, it.ldx, 1, hadamard, a.rounding, a.layout, a.q,
+                                 a.ldq, a.scales, a.lds)) != MXFP4_OK)
+            return st;
+        if ((st = check_quantize(it.x, it.dtype, it.rows, it.cols, it.ldx, 0, hadamard, b.rounding, b.layout, b.q,
+                                 b.ldq, b.scales, b.lds)) != MXFP4_OK)
+            return st;
+        any = any || (it.rows > 0 && it.cols > 0);
+    }
+    if (!any) return MXFP4_OK;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    const auto conv = [](const mxfp4_quant_out_t &o) {
+        return mx::QuantOut{is_sr(o.rounding), is_noclip(o.rounding), o.seed, o.stream_id,
+                            o.layout == MXFP4_LAYOUT_TILED, o.q, o.ldq, o.scales, o.lds};
+    };
+    mx::DualInput in[MXFP4_DUAL_GROUP_MAX];
+    for (int i = 0; i < count; ++i)
+        in[i] = mx::DualInput{items[i].x, items[i].rows, items[i].cols, items[i].ldx, conv(items[i].axis1),
+                              conv(items[i].axis0)};
+    return from_hip(mx::launch_quantize_dual_grouped(in, count, items[0].dtype == MXFP4_IN_F32, hadamard,
+                                                     (hipStream_t)stream));
+}
+
 mxfp4_status_t mxfp4_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_t ldas,
                           const uint8_t *bq, int64_t ldb, const uint8_t *bs, int64_t ldbs,
                           int64_t M, int64_t N, int64_t K, float alpha, float *c, int64_t ldc,

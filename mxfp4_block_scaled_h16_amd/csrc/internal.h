@@ -44,6 +44,17 @@ hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t c
                                 int hadamard, const QuantOut &axis1, const QuantOut &axis0,
                                 hipStream_t stream);
 
+// Several tensors' dual quantizations in one launch (one element type and rotation, up to 8
+// tensors of any shapes): every tensor's 128 x 128 tiles are workgroups of the same grid.
+constexpr int kDualGroupMax = 8;
+struct DualInput {
+    const void *x;
+    int64_t rows, cols, ldx;
+    QuantOut axis1, axis0;
+};
+hipError_t launch_quantize_dual_grouped(const DualInput *items, int count, bool f32, int hadamard,
+                                        hipStream_t stream);
+
 // tiled: both operands in the tiled layout (K % 512 == 0, rows padded to multiples of 256);
 // otherwise row-major with leading dimensions. A workspace of gemm_workspace_bytes() bytes
 // (16-byte aligned) lets a GEMM with few output tiles split K (gemm_splits() ways) into FP32

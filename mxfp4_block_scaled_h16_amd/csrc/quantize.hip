@@ -365,10 +365,20 @@ struct DualOut {
     uint32_t sr, tiled, noclip;
 };
 
+// One tensor of a grouped launch: its tiles are workgroups [tile0, tile0 + row tiles x col_tiles).
+struct DualItem {
+    const void *x;
+    int64_t ldx;
+    uint32_t rows, cols, col_tiles, tile0;
+    DualOut o1, o0;
+};
+struct DualGroup {
+    DualItem item[kDualGroupMax];
+    int count;
+};
+
 template <int H, bool F32, bool RHT, int NW>
-__global__ __launch_bounds__(64 * NW) void quant_dual_kernel(
-    const void *__restrict__ x, int64_t ldx, uint32_t rows, uint32_t cols, uint32_t col_tiles,
-    DualOut o1, DualOut o0, float norm)
+__global__ __launch_bounds__(64 * NW) void quant_dual_kernel(DualGroup grp, float norm)
 {
     static_assert(NW == 4 || NW == 8, "four or eight wavefronts");
     constexpr int kEsize = F32 ? 4 : 2;
@@ -381,9 +391,20 @@ __global__ __launch_bounds__(64 * NW) void quant_dual_kernel(
     uint8_t *out = tile;                          // reused once the tile has been read
     uint8_t *out_scales = tile + kDualTile * 64;
 
+    // the tensor of this workgroup: the last one whose first tile is at or below blockIdx.x (a
+    // tensor without tiles shares its first tile with the next one)
+    int it = 0;
+    for (int i = 1; i < grp.count; ++i)
+        if (blockIdx.x >= grp.item[i].tile0) it = i;
+    const void *__restrict__ x = grp.item[it].x;
+    const int64_t ldx = grp.item[it].ldx;
+    const uint32_t rows = grp.item[it].rows, cols = grp.item[it].cols, col_tiles = grp.item[it].col_tiles;
+    const DualOut o1 = grp.item[it].o1, o0 = grp.item[it].o0;
+    const uint32_t t_index = blockIdx.x - grp.item[it].tile0;
+
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t c0 = (blockIdx.x % col_tiles) * kDualTile;
-    const uint32_t r0 = (blockIdx.x / col_tiles) * kDualTile;
+    const uint32_t c0 = (t_index % col_tiles) * kDualTile;
+    const uint32_t r0 = (t_index / col_tiles) * kDualTile;
     const uint32_t nrows = min((uint32_t)kDualTile, rows - r0);  // multiples of 32
     const uint32_t ncols = min((uint32_t)kDualTile, cols - c0);
     const char *xb = reinterpret_cast<const char *>(x);
@@ -590,14 +611,10 @@ __global__ __launch_bounds__(64 * NW) void quant_dual_kernel(
 }
 
 template <int H, bool F32, bool RHT>
-hipError_t dual_dispatch(const void *x, int64_t rows, int64_t cols, int64_t ldx, const DualOut &o1,
-                         const DualOut &o0, float norm, hipStream_t stream)
+hipError_t dual_dispatch(const DualGroup &grp, uint32_t tiles, float norm, hipStream_t stream)
 {
-    const int64_t col_tiles = (cols + kDualTile - 1) / kDualTile;
-    const int64_t row_tiles = (rows + kDualTile - 1) / kDualTile;
-    return launch(quant_dual_kernel<H, F32, RHT, kDualWaves>, dim3((unsigned)(col_tiles * row_tiles)),
-                  dim3(64 * kDualWaves), 0, stream, x, ldx, (uint32_t)rows, (uint32_t)cols, (uint32_t)col_tiles,
-                  o1, o0, norm);
+    return launch(quant_dual_kernel<H, F32, RHT, kDualWaves>, dim3(tiles), dim3(64 * kDualWaves), 0, stream, grp,
+                  norm);
 }
 
 template <int H, bool F32, bool SR, bool TILED, bool RHT>
@@ -699,30 +716,51 @@ hipError_t launch_quantize_cols(const void *x, bool f32, int64_t rows, int64_t c
                          stream);
 }
 
-hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
-                                int hadamard, const QuantOut &axis1, const QuantOut &axis0,
-                                hipStream_t stream)
+hipError_t launch_quantize_dual_grouped(const DualInput *items, int count, bool f32, int hadamard,
+                                        hipStream_t stream)
 {
+    if (count < 1 || count > kDualGroupMax) return hipErrorInvalidValue;
     const auto conv = [](const QuantOut &o) {
         return DualOut{o.q, o.ldq, o.scales, o.lds, (uint32_t)o.seed, (uint32_t)(o.seed >> 32), o.stream_id,
                        o.stochastic ? 1u : 0u, o.tiled ? 1u : 0u, o.noclip ? 1u : 0u};
     };
-    const DualOut o1 = conv(axis1), o0 = conv(axis0);
+    DualGroup grp{};
+    grp.count = count;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        const DualInput &d = items[i];
+        const int64_t col_tiles = (d.cols + kDualTile - 1) / kDualTile;
+        const int64_t row_tiles = (d.rows + kDualTile - 1) / kDualTile;
+        grp.item[i] = DualItem{d.x, d.ldx, (uint32_t)d.rows, (uint32_t)d.cols, (uint32_t)col_tiles, (uint32_t)tiles,
+                               conv(d.axis1), conv(d.axis0)};
+        tiles += d.rows > 0 && d.cols > 0 ? col_tiles * row_tiles : 0;
+    }
+    if (tiles == 0) return hipSuccess;
+    if (tiles > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
     const float norm = rotation_norm(hadamard);
     const bool rht = (hadamard & kRandomizedHadamard) != 0;
+    const uint32_t n = (uint32_t)tiles;
     switch ((hadamard & kHadamardSize) * 4 + (f32 ? 2 : 0) + (rht ? 1 : 0)) {
-    case 0: return dual_dispatch<0, false, false>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 2: return dual_dispatch<0, true, false>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 64: return dual_dispatch<16, false, false>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 65: return dual_dispatch<16, false, true>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 66: return dual_dispatch<16, true, false>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 67: return dual_dispatch<16, true, true>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 128: return dual_dispatch<32, false, false>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 129: return dual_dispatch<32, false, true>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 130: return dual_dispatch<32, true, false>(x, rows, cols, ldx, o1, o0, norm, stream);
-    case 131: return dual_dispatch<32, true, true>(x, rows, cols, ldx, o1, o0, norm, stream);
+    case 0: return dual_dispatch<0, false, false>(grp, n, norm, stream);
+    case 2: return dual_dispatch<0, true, false>(grp, n, norm, stream);
+    case 64: return dual_dispatch<16, false, false>(grp, n, norm, stream);
+    case 65: return dual_dispatch<16, false, true>(grp, n, norm, stream);
+    case 66: return dual_dispatch<16, true, false>(grp, n, norm, stream);
+    case 67: return dual_dispatch<16, true, true>(grp, n, norm, stream);
+    case 128: return dual_dispatch<32, false, false>(grp, n, norm, stream);
+    case 129: return dual_dispatch<32, false, true>(grp, n, norm, stream);
+    case 130: return dual_dispatch<32, true, false>(grp, n, norm, stream);
+    case 131: return dual_dispatch<32, true, true>(grp, n, norm, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_quantize_dual(const void *x, bool f32, int64_t rows, int64_t cols, int64_t ldx,
+                                int hadamard, const QuantOut &axis1, const QuantOut &axis0,
+                                hipStream_t stream)
+{
+    const DualInput one{x, rows, cols, ldx, axis1, axis0};
+    return launch_quantize_dual_grouped(&one, 1, f32, hadamard, stream);
 }
 
 }  // namespace mx

@@ -68,6 +68,29 @@ int main(void)
     o0.rounding = (mxfp4_rounding_t)9;
     EXPECT(mxfp4_quantize_dual(p, MXFP4_IN_BF16, 64, 64, 64, 16, &o1, &o0, NULL), MXFP4_ERR_ARG);
 
+    /* grouped dual quantize */
+    mxfp4_dual_item_t di[MXFP4_DUAL_GROUP_MAX + 1];
+    for (int i = 0; i <= MXFP4_DUAL_GROUP_MAX; ++i) {
+        di[i].x = p; di[i].dtype = MXFP4_IN_BF16; di[i].rows = 64; di[i].cols = 64; di[i].ldx = 64;
+        di[i].axis1 = o1; di[i].axis0 = o1;
+    }
+    EXPECT(mxfp4_quantize_dual_grouped(di, MXFP4_DUAL_GROUP_MAX + 1, 16, NULL), MXFP4_ERR_ARG);
+    EXPECT(mxfp4_quantize_dual_grouped(di, -1, 16, NULL), MXFP4_ERR_ARG);
+    EXPECT(mxfp4_quantize_dual_grouped(NULL, 2, 16, NULL), MXFP4_ERR_NULL);
+    EXPECT(mxfp4_quantize_dual_grouped(NULL, 0, 16, NULL), MXFP4_OK);
+    di[1].dtype = MXFP4_IN_F32;
+    EXPECT(mxfp4_quantize_dual_grouped(di, 2, 16, NULL), MXFP4_ERR_ARG);          /* mixed dtypes */
+    di[1].dtype = MXFP4_IN_BF16;
+    di[1].rows = 48;
+    EXPECT(mxfp4_quantize_dual_grouped(di, 2, 16, NULL), MXFP4_ERR_SHAPE);        /* rows % 32 */
+    di[1].rows = 64;
+    EXPECT(mxfp4_quantize_dual_grouped(di, 2, 24, NULL), MXFP4_ERR_ARG);          /* hadamard size */
+    di[1].axis0.q = NULL;
+    EXPECT(mxfp4_quantize_dual_grouped(di, 2, 16, NULL), MXFP4_ERR_NULL);
+    di[1].axis0.q = q;
+    di[0].rows = 0; di[1].rows = 0;
+    EXPECT(mxfp4_quantize_dual_grouped(di, 2, 16, NULL), MXFP4_OK);               /* nothing to do */
+
     /* gemm and gemm_ex */
     EXPECT(mxfp4_gemm(q, 32, q, 2, q, 32, q, 2, 8, 8, 48, 1.0f, c, 8, MXFP4_LAYOUT_ROWS, NULL, 0, NULL),
            MXFP4_ERR_SHAPE);                                     /* K not a multiple of 32 */

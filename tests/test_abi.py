@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                      "mxfp4_abi_version"):
         assert expected in names
     assert "mxfp4_tiled_sizes" in names and "mxfp4_gemm_workspace_bytes" in names
-    assert "mxfp4_gemm_grouped" in names
+    assert "mxfp4_gemm_grouped" in names and "mxfp4_quantize_dual_grouped" in names
     assert "mxfp4_quantize_dual" in names
     assert {"mxfp4_linear_forward", "mxfp4_linear_backward", "mxfp4_linear_step_workspace_bytes"} <= set(names)
 
@@ -64,7 +64,7 @@ def test_ceiling_library_exports_its_declared_symbols():
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 11
+    assert L.mxfp4_abi_version() == 12
     for st in range(8):
         assert L.mxfp4_status_string(st)
     assert L.mxfp4_status_string(0) == b"ok"

@@ -80,7 +80,7 @@ def test_counter_summaries_are_ignored_once_the_source_changes(tmp_path, monkeyp
     (prof / "quant_layer_step_sq_counters.txt").write_text(
         "# test\nsource_digest: %s\nlaunch | waves | valu_per_wave\nquant_dual x | 100 | 2000\n" % digest)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    plan = types.SimpleNamespace(op_list=[("quant_dual x", "dual", ((0, 0, 0, 1, "rne"), (0, 0, 0, 0, "sr")), 0)])
+    plan = types.SimpleNamespace(op_list=[("quant_dual x", "dual", (((0, 0, 0, 1, "rne"), (0, 0, 0, 0, "sr")),), 0)])
     v = bench.quantizer_valu("layer", plan, [0.01])
     assert v["launches"]["quant_dual x"]["valu_giga_lane_ops"] == round(100 * 2000 * 64 / 1e9, 2)
     assert abs(v["frac"] - 100 * 2000 * 64 / 1e-5 / bench.VALU_LANE_OPS_PEAK) < 1e-3
@@ -90,9 +90,10 @@ def test_counter_summaries_are_ignored_once_the_source_changes(tmp_path, monkeyp
 
 def test_layer_plan_groups_same_shape_products():
     """The layer's launch list: k and v, and gate and up, read one input with weights of one
-    shape, so each of their passes is one grouped launch (15 GEMM launches for 21 products);
-    without grouping there is one launch per product. Every product appears once, and every
-    quantized operand is produced by an earlier launch than the GEMM that reads it."""
+    shape, so each of their passes is one grouped launch (15 GEMM launches for 21 products), and
+    dual quantizations that run back to back share one launch; without grouping there is one
+    launch per product and per tensor. Every product appears once, and every quantized operand is
+    produced by an earlier launch than the GEMM that reads it."""
     sys.path.insert(0, ROOT)
     import bench
 
@@ -110,7 +111,7 @@ def test_layer_plan_groups_same_shape_products():
         made = set()
         for label, kind, spec, work in ops:
             if kind == "dual":
-                made.update(q[7] for q in spec)
+                made.update(q[7] for pair in spec for q in pair)
             elif kind == "quant":
                 made.add(spec[7])
             else:
@@ -120,3 +121,9 @@ def test_layer_plan_groups_same_shape_products():
                 assert len(shapes) == 1, label
         if group:
             assert [len(op[2]) for op in gemms] == [1, 1, 1, 2, 2, 2, 1, 1, 1, 2, 2, 2, 1, 1, 1]
+        # dual launches: one per tensor (18) or, grouped, runs of back-to-back ones merged
+        duals = [op for op in ops if op[1] == "dual"]
+        assert sum(len(op[2]) for op in duals) == 18
+        assert len(duals) == (10 if group else 18)
+        if group:
+            assert all(ops[i][1] != "dual" or ops[i + 1][1] != "dual" for i in range(len(ops) - 1))

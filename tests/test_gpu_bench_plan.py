@@ -23,7 +23,7 @@ def _oracle_operands(plan, h):
     acts, per_proj = plan.host["acts"], plan.host["proj"]
     ops = {}
     for label, kind, spec, work in plan.op_list:
-        specs = spec if kind == "dual" else (spec,) if kind == "quant" else ()
+        specs = [q for pair in spec for q in pair] if kind == "dual" else (spec,) if kind == "quant" else ()
         for _, src, key, axis, rnd, seed, stream, dst, _ in specs:
             t = acts[key] if src == "act" else per_proj[key][0 if src == "w" else 1]
             r = oracle.SR if rnd == "sr" else oracle.RNE
