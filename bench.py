@@ -241,18 +241,28 @@ class Plan:
                 emit(qb)
             ops.append((label, "gemm", tuple(prods), flops))
         if self.group:
-            # dual quantizations that run back to back (an activation and the weight of the
-            # product that reads it, k and v, gate and up) share one launch
+            # launches that run back to back share one: dual quantizations (an activation and the
+            # weight of the product that reads it, k and v, gate and up), and GEMMs of one output
+            # shape and contraction (the Dgrad and Wgrad of a layer with as many tokens as outputs)
             merged = []
             for op in ops:
                 last = merged[-1] if merged else None
-                if op[1] == "dual" and last is not None and last[1] == "dual" and len(last[2]) + len(op[2]) <= 8:
-                    merged[-1] = (last[0] + "+" + op[0][len("quant_dual "):], "dual", last[2] + op[2],
-                                  last[3] + op[3])
+                same = last is not None and last[1] == op[1] and len(last[2]) + len(op[2]) <= 8 and (
+                    op[1] == "dual" or (op[1] == "gemm" and self.gemm_shape(last[2][0][2]) ==
+                                        self.gemm_shape(op[2][0][2])))
+                if same:
+                    prefix = "quant_dual " if op[1] == "dual" else "gemm "
+                    merged[-1] = (last[0] + "+" + op[0][len(prefix):], op[1], last[2] + op[2], last[3] + op[3])
                 else:
                     merged.append(op)
             ops = merged
         self.op_list = ops
+
+    def gemm_shape(self, okey):
+        """(output rows, output columns, contraction) of the GEMM that writes okey."""
+        name, pas = okey
+        K, N = next((k, n) for nm, k, n in self.projs if nm == name)
+        return {"F": (self.M, N, K), "D": (self.M, K, N), "W": (N, K, self.M)}[pas]
 
     def _tensor(self, d_acts, d_proj, q):
         src, key = q[1], q[2]

@@ -140,16 +140,36 @@ constexpr int kEpiBF16 = 2;     // bf16 with beta
 // Workgroup tile 128 x 128, four wavefronts in a 2 x 2 arrangement, each 64 x 64 (2 x 2 MFMA
 // tiles of 32 x 32); one K step = 64 (two MX blocks per row).
 constexpr int kTileM = 128, kTileN = 128, kWaveM = 64, kWaveN = 64;
+constexpr int kGroupMax = 8;                          // products of one grouped launch
+
+// The products of a grouped launch: same shapes, strides and layout, operands and outputs of
+// their own.
+struct GroupItem {
+    const uint8_t *aq, *as, *bq, *bs;
+    float *c;
+};
+struct GroupArgs {
+    GroupItem item[kGroupMax];
+    int count;
+};
 
 // FOLD: the accumulation chain restarts from zero every fold_steps MFMA steps, the finished
 // segments summed in K order in a second set of registers (contractions longer than one chain
-// may be).
+// may be). A grouped launch (grp.count > 0) runs product blockIdx.z of grp.
 template <bool FOLD>
 __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
-    int M, int N, int K, OutSpec out, int fold_steps)
+    int M, int N, int K, OutSpec out, int fold_steps, GroupArgs grp)
 {
+    if (grp.count > 0) {
+        const GroupItem &it = grp.item[blockIdx.z];
+        aq = it.aq;
+        as = it.as;
+        bq = it.bq;
+        bs = it.bs;
+        out.c = it.c;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int m_base = blockIdx.y * kTileM + (wave >> 1) * kWaveM;
@@ -279,7 +299,6 @@ constexpr int kRowBytes = kStageK / 2;                // 64 bytes of codes per r
 constexpr int kNumBuf = 4;                            // stage ring; a group = 4 stages
 constexpr int kRowsPerDma = 1024 / kRowBytes;         // one wave-wide 16 B/lane DMA covers 16 rows
 constexpr int kGemmWaves = 8;                         // wavefronts per workgroup (4 or 8)
-constexpr int kGroupMax = 8;                          // products of one grouped launch
 // the tile of products whose contraction needs a segmented accumulation chain: 256 x 128, eight
 // wavefronts of 64 x 64 (a 128 x 64 wave tile has no registers left for the second accumulator
 // set). Measured against four wavefronts of 128 x 64 (one per SIMD, 455 registers): the same
@@ -335,17 +354,6 @@ struct Geo {
     static constexpr int kScaleChunks = (TM + TN) / 64;           // 64-row scale DMAs per group
     static constexpr int kDmaPerScales = (kScaleChunks + NW - 1) / NW;  // per wavefront and group
     static constexpr int kMinBlocks = kLdsBytes <= 80 * 1024 ? 2 : 1;   // workgroups per CU
-};
-
-// The products of a grouped launch: same shapes, strides and layout, operands and outputs of
-// their own.
-struct GroupItem {
-    const uint8_t *aq, *as, *bq, *bs;
-    float *c;
-};
-struct GroupArgs {
-    GroupItem item[kGroupMax];
-    int count;
 };
 
 // EPI: kEpiF32 writes FP32 c = alpha * A B^T (out.c a float pointer; no other epilogue code is
@@ -831,9 +839,9 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
         const int fold_steps = chain_segment((K + 63) / 64, 2);
         if (fold_steps > 0)
             return launch(gemm_mxfp4_simple<true>, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs,
-                          ldbs, (int)M, (int)N, (int)K, out, fold_steps);
+                          ldbs, (int)M, (int)N, (int)K, out, fold_steps, GroupArgs{});
         return launch(gemm_mxfp4_simple<false>, sgrid, dim3(256), 0, stream, aq, lda, as, ldas, bq, ldb, bs, ldbs,
-                      (int)M, (int)N, (int)K, out, 0);
+                      (int)M, (int)N, (int)K, out, 0, GroupArgs{});
     }
     int splits = gemm_splits(M, N, K);
     if (splits > 1 && (workspace == nullptr || ws_bytes < gemm_workspace_bytes(M, N, K) ||
@@ -906,8 +914,8 @@ hipError_t launch_gemm_grouped(const GemmGroupItem *items, int count, int64_t ld
     bool pipelined = tiled || (K % 512 == 0 && K > 0 && scales_aligned && offsets_fit);
     for (int i = 0; i < count; ++i)
         pipelined = pipelined && ((uintptr_t)items[i].as % 16 == 0) && ((uintptr_t)items[i].bs % 16 == 0);
-    if (!pipelined || count > kGroupMax) {
-        // the row kernel, product by product
+    if (count > kGroupMax) {
+        // product by product
         for (int i = 0; i < count; ++i) {
             const hipError_t e = launch_gemm(items[i].aq, lda, items[i].as, ldas, items[i].bq, ldb, items[i].bs,
                                              ldbs, M, N, K, alpha, 0.0f, items[i].c, false, ldc, tiled, nullptr, 0,
@@ -921,6 +929,17 @@ hipError_t launch_gemm_grouped(const GemmGroupItem *items, int count, int64_t ld
     for (int i = 0; i < count; ++i)
         grp.item[i] = GroupItem{items[i].aq, items[i].as, items[i].bq, items[i].bs, items[i].c};
     const OutSpec out{items[0].c, ldc, alpha, 0.0f, 0};
+    if (!pipelined) {
+        // the row kernel, one grid layer per product
+        const dim3 sgrid((unsigned)((N + kTileN - 1) / kTileN), (unsigned)((M + kTileM - 1) / kTileM),
+                         (unsigned)count);
+        const int fold_steps = chain_segment((K + 63) / 64, 2);
+        if (fold_steps > 0)
+            return launch(gemm_mxfp4_simple<true>, sgrid, dim3(256), 0, stream, items[0].aq, lda, items[0].as, ldas,
+                          items[0].bq, ldb, items[0].bs, ldbs, (int)M, (int)N, (int)K, out, fold_steps, grp);
+        return launch(gemm_mxfp4_simple<false>, sgrid, dim3(256), 0, stream, items[0].aq, lda, items[0].as, ldas,
+                      items[0].bq, ldb, items[0].bs, ldbs, (int)M, (int)N, (int)K, out, 0, grp);
+    }
     const int fold = chain_segment(K / 512, 16);
     const int64_t big_tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN) * count;
     // the geometry launch_gemm would pick for one product with all the products' tiles

@@ -80,12 +80,14 @@ def test_qkv_step_sampled():
 @pytest.mark.parametrize("group", [True, False])
 def test_layer_step_sampled(group):
     """The decoder-layer step the benchmark times, at 1024 tokens (the 7 projections' weights
-    at full size): k and v, gate and up each run as one grouped launch per pass (or one launch per
-    product), dual quantizers with SR on the Wgrad operands. 1024 sampled outputs per product
-    plus the corners, against the oracle."""
+    at full size): k and v, gate and up each run as one grouped launch per pass, and adjacent
+    launches of one shape merge (or one launch per product), dual quantizers with SR on the Wgrad
+    operands. 1024 sampled outputs per product plus the corners, against the oracle."""
     plan = _run_plan("layer", 16, True, group=group, tokens=1024)
     n_launch = sum(1 for _, kind, _, _ in plan.op_list if kind == "gemm")
-    assert n_launch == (15 if group else 21)
+    n_products = sum(len(spec) for _, kind, spec, _ in plan.op_list if kind == "gemm")
+    # at 1024 tokens the k/v Dgrad and Wgrad (both 1024 x 4096 over 1024) join the k/v group too
+    assert n_products == 21 and n_launch == (14 if group else 21)
     _check_outputs(plan, 16, samples=1024)
 
 
