@@ -354,6 +354,19 @@ def measured_traffic(workload):
 VALU_LANE_OPS_PEAK = 256 * 4 * 32 * 2.4e9
 
 
+def measured_mfma_busy(workload):
+    """The fraction of SIMD cycles the matrix cores were busy during the step's GEMM launches
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs), from the committed SQ summary
+    of this workload, if it was taken with the GEMM source as it is now (otherwise None)."""
+    got = _profile_values("gemm_mxfp4_%s_step_sq_counters.txt" % workload, "gemm.hip")
+    if got is None:
+        return None
+    try:
+        return float(got[0]["mfma_busy_step"])
+    except (KeyError, ValueError):
+        return None
+
+
 def quantizer_valu(workload, plan, avg_ms):
     """The stochastic-rounding quantizer launches against the VALU roofline: VALU instructions
     per wavefront and wavefronts per launch from the committed SQ counter summary of this
@@ -862,6 +875,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MXFP4_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MXFP4_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(args.workload),
+                "mfma_busy": measured_mfma_busy(args.workload),
                 "kernel": "gemm_mxfp4_pipelined (%d launches per step; achieved = GEMM FLOPs / GEMM time)" % n_gemm,
                 "algorithmic_per_launch": "2*M*N*K = %.1f GFLOP average" % (gemm_flops / n_gemm / 1e9),
                 "algorithmic_bytes_per_launch": int(gemm_bytes / n_gemm)}
