@@ -443,6 +443,18 @@ def quantization_error(plan, rows=8):
 GEMM_ROWS = 1024  # output rows of the oracle GEMM the CPU baseline times (about 15 s on 16 cores)
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(plan, h):
     """The oracle, untuned, on a bounded sample of the same step, projected to the whole step."""
     import numpy as np
@@ -490,6 +502,7 @@ def cpu_baseline(plan, h):
                                  c.shape[0], name0)),
             "cpu_seconds": round(time.perf_counter() - t_begin, 2),
             "gemm_gflops": rate_gemm / 1e9, "quantize_melem_s": rate_rows / 1e6,
+            "quantize_gbs": rate_rows * QUANT_BYTES_PER_ELEM / 1e9, "cpu_model": cpu_model(),
             "step_seconds_projected": t_step}
 
 
