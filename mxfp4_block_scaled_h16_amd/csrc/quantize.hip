@@ -2,12 +2,15 @@
 //
 // The operand transform of the gist.science summary of "MXFP4 LLM pretraining", section 방법론
 // (Methodology): deterministic block Hadamard (H16 / H32) along the GEMM's contraction axis, then
-// MXFP4 quantization with nearest-even or stochastic rounding. Two kernels:
+// MXFP4 quantization with nearest-even or stochastic rounding. Three kernels:
 //   quant_rows -- along the contiguous axis (Fprop operands, the Dgrad gradient operand);
 //   quant_cols -- along the strided axis, writing the quantized transpose (the Wgrad token axis,
-//                 section "주요 기여 및 발견" §1: the weight gradient is where MXFP4 hurts most).
-// Both are HBM-bound: 2 bytes read and 0.5 + 1/32 bytes written per bf16 element; nearest-even
-// rounding uses the hardware FP4 conversion, stochastic rounding a Philox word per element.
+//                 section "주요 기여 및 발견" §1: the weight gradient is where MXFP4 hurts most);
+//   quant_dual -- both from one read of the tensor, for up to 8 tensors per launch.
+// Their bound is HBM: 2 bytes read and 0.5 + 1/32 bytes written per bf16 element (both axes:
+// 2 + 2 x (0.5 + 1/32)); nearest-even rounding uses the hardware FP4 conversion, stochastic
+// rounding a Philox word per element, whose 64-bit multiply-adds make those launches partly
+// VALU-bound.
 #include "internal.h"
 #include "mx_device.h"
 
