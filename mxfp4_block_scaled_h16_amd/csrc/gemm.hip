@@ -356,6 +356,19 @@ struct Geo {
     static constexpr int kMinBlocks = kLdsBytes <= 80 * 1024 ? 2 : 1;   // workgroups per CU
 };
 
+// where a virtual block of the pipelined kernel works: its K-split, tile origin, operands, output
+struct TileWhere {
+    int split, m0, n0;
+    const uint8_t *aq, *as, *bq, *bs;
+    void *c;
+};
+// a lane's DMA source offsets for one tile: codes of A and B, scales (and their operand)
+template <int DA, int DB, int DS>
+struct DmaOffsets {
+    uint32_t a[DA], b[DB], s[DS];
+    const uint8_t *src[DS];
+};
+
 // EPI: kEpiF32 writes FP32 c = alpha * A B^T (out.c a float pointer; no other epilogue code is
 // compiled in), kEpiF32Beta adds beta * c, kEpiBF16 writes bf16 (with beta * c).
 // GROUP: the grid covers grp.count products (FP32 output, no split of K), one after another in
@@ -363,7 +376,11 @@ struct Geo {
 // FOLD: the accumulation chain restarts from zero every fold_groups groups of four stages, the
 // finished segments summed in K order in a second set of registers (contractions longer than
 // one chain may be; only geometries with 64 x 64 wave tiles have the registers for it).
-template <int NW, bool TILED, int EPI, int TM = kBM, int TN = kBN, int WM = 2, bool FOLD = false, bool GROUP = false>
+// PERSIST: a grid of at most one workgroup per CU walks the tiles (virtual block blockIdx.x, then
+// + gridDim.x, ...), and the first two stages and scales of its next tile are loaded during the
+// last stages of the current one (FP32 output, unsplit, an even number of groups).
+template <int NW, bool TILED, int EPI, int TM = kBM, int TN = kBN, int WM = 2, bool FOLD = false, bool GROUP = false,
+          bool PERSIST = false>
 __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void gemm_mxfp4_pipelined(
     const uint8_t *__restrict__ aq, int64_t lda, const uint8_t *__restrict__ as, int64_t ldas,
     const uint8_t *__restrict__ bq, int64_t ldb, const uint8_t *__restrict__ bs, int64_t ldbs,
@@ -373,10 +390,19 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
     static_assert(!GROUP || EPI == kEpiF32, "grouped products write FP32 without beta");
     using G = Geo<NW, TM, TN, WM>;
     static_assert(!FOLD || G::FI * G::FJ <= 4, "segmented accumulation needs wave tiles of at most 64 x 64");
+    static_assert(!PERSIST || EPI == kEpiF32, "the persistent walk writes FP32 without beta");
     constexpr int FI = G::FI, FJ = G::FJ;
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes, kScaleSlot = G::kScaleSlot;
-    constexpr int kScaleBase = G::kScaleBase;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::kLdsBytes];
+    // LDS: the stage ring, then the two scale slots. The walk puts the scale slots first, so that
+    // ring buffers 2 and 3 and the space after them hold the epilogue's 32-row slices (unpadded,
+    // one per wavefront) while the next tile's first stages land in buffers 0 and 1.
+    constexpr int kRingBase = PERSIST ? 2 * kScaleSlot : 0;
+    constexpr int kScaleBase = PERSIST ? 0 : G::kScaleBase;
+    constexpr int kSliceOut = kRingBase + 2 * kStageBytes;
+    constexpr int kWalkLds = kSliceOut + NW * 32 * G::kWaveCols * 4;
+    constexpr int kLdsBytes = PERSIST && kWalkLds > G::kLdsBytes ? kWalkLds : G::kLdsBytes;
+    static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
     // tile order: consecutive workgroups are spread over the 8 XCDs; give each XCD a contiguous
     // range of tiles, walked column-panel by column-panel in groups of row panels, so that one
@@ -385,33 +411,48 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
     // fetch 20% fewer operand bytes per round than 8 x 4; measured 1-1.5% faster on the
     // segmented-chain products of the decoder layer, 4.025 -> 4.006 ms per step)
     const int total = tiles_m * tiles_n;
-    int split, t;
-    if constexpr (GROUP) {
-        // the products' tiles as one range spread over the XCDs, product by product
-        const int all = total * grp.count;
-        int u = blockIdx.x;
-        if (all % 8 == 0) u = (u % 8) * (all / 8) + u / 8;
-        const int gi = u / total;
-        t = u % total;
-        split = 0;
-        aq = grp.item[gi].aq;
-        as = grp.item[gi].as;
-        bq = grp.item[gi].bq;
-        bs = grp.item[gi].bs;
-        out.c = grp.item[gi].c;
-    } else {
-        // split-K: workgroup blockIdx.x covers K-split blockIdx.x / total of tile blockIdx.x % total
-        split = blockIdx.x / total;
-        t = blockIdx.x % total;
-        if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;
-    }
     constexpr int kGroupRows = 8 * TN / TM;   // a round of 32 tiles covers about a square region
-    const int group = kGroupRows * tiles_n;
-    const int g0 = (t / group) * kGroupRows;
-    const int gm = min(kGroupRows, tiles_m - g0);
-    const int tm = g0 + (t % group) % gm;
-    const int tn = (t % group) / gm;
-    const int m0 = tm * TM, n0 = tn * TN;
+    // virtual block v: its K-split, tile origin and (grouped) the product's operands and output
+    auto locate = [&](int v) {
+        TileWhere w;
+        int t;
+        if constexpr (GROUP) {
+            // the products' tiles as one range spread over the XCDs, product by product
+            const int all = total * grp.count;
+            int u = v;
+            if (all % 8 == 0) u = (u % 8) * (all / 8) + u / 8;
+            const int gi = u / total;
+            t = u % total;
+            w.split = 0;
+            w.aq = grp.item[gi].aq;
+            w.as = grp.item[gi].as;
+            w.bq = grp.item[gi].bq;
+            w.bs = grp.item[gi].bs;
+            w.c = grp.item[gi].c;
+        } else {
+            // split-K: block v covers K-split v / total of tile v % total (the walk never splits)
+            w.split = PERSIST ? 0 : v / total;
+            t = PERSIST ? v : v % total;
+            if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;
+            w.aq = aq;
+            w.as = as;
+            w.bq = bq;
+            w.bs = bs;
+            w.c = out.c;
+        }
+        const int group = kGroupRows * tiles_n;
+        const int g0 = (t / group) * kGroupRows;
+        const int gm = min(kGroupRows, tiles_m - g0);
+        w.m0 = (g0 + (t % group) % gm) * TM;
+        w.n0 = ((t % group) / gm) * TN;
+        return w;
+    };
+    int vblock = blockIdx.x;
+    TileWhere cur = locate(vblock);
+    int split = cur.split, m0 = cur.m0, n0 = cur.n0;
+    aq = cur.aq;
+    bq = cur.bq;
+    out.c = cur.c;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -426,53 +467,62 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
     const int a_row0 = kRowsPerDma * G::kDmaA * wave;
     const int b_row0 = kRowsPerDma * G::kDmaB * wave;
     const uint32_t kblocks = (uint32_t)(K / kStageK);
-    uint32_t a_off[G::kDmaA], b_off[G::kDmaB];
-#pragma unroll
-    for (int u = 0; u < G::kDmaA; ++u) {
-        if constexpr (TILED) {
-            const uint32_t rb = (uint32_t)(m0 + a_row0 + kRowsPerDma * u) / 16;
-            a_off[u] = rb * kblocks * 1024u + (uint32_t)lane * 16u;
-        } else {
-            const int row = a_row0 + kRowsPerDma * u + lane / 4;
-            const int chunk = (lane % 4) ^ chunk_perm(row);
-            a_off[u] = (uint32_t)(min(m0 + row, M - 1) * lda + 16 * chunk);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < G::kDmaB; ++u) {
-        if constexpr (TILED) {
-            const uint32_t rb = (uint32_t)(n0 + b_row0 + kRowsPerDma * u) / 16;
-            b_off[u] = rb * kblocks * 1024u + (uint32_t)lane * 16u;
-        } else {
-            const int row = b_row0 + kRowsPerDma * u + lane / 4;
-            const int chunk = (lane % 4) ^ chunk_perm(row);
-            b_off[u] = (uint32_t)(min(n0 + row, N - 1) * ldb + 16 * chunk);
-        }
-    }
     // scale DMA: 64 rows of one operand per instruction, 16 bytes (one group) per lane. The
     // tile's 64-row chunks (A's first, then B's) go round-robin over the wavefronts: instruction u
     // of wavefront w brings chunk (w + NW u) mod kScaleChunks. Where the chunks do not divide
     // evenly, the last wavefronts load a chunk a second time (the same bytes to the same place),
     // so that every wavefront issues the same number of loads and its vmcnt waits count alike.
-    uint32_t s_off[G::kDmaPerScales];
     int s_dst[G::kDmaPerScales];
-    const uint8_t *s_src[G::kDmaPerScales];
 #pragma unroll
     for (int u = 0; u < G::kDmaPerScales; ++u) {
         const int chunk = (wave + NW * u) % G::kScaleChunks;
         const bool is_b = chunk >= TM / 64;
-        const int q64 = is_b ? chunk - TM / 64 : chunk;
-        const int row = 64 * q64 + lane;
-        s_src[u] = is_b ? bs : as;
-        if constexpr (TILED) {
-            // 64-row x 512-K scale blocks of 1024 bytes, 16 per row
-            s_off[u] = ((uint32_t)(is_b ? n0 : m0) / 64 + (uint32_t)q64) * ((uint32_t)K / 512) * 1024u +
-                       (uint32_t)lane * 16u;
-        } else {
-            s_off[u] = (uint32_t)(is_b ? min(n0 + row, N - 1) * ldbs : min(m0 + row, M - 1) * ldas);
-        }
-        s_dst[u] = (is_b ? TM * 16 : 0) + 1024 * q64;
+        s_dst[u] = (is_b ? TM * 16 : 0) + 1024 * (is_b ? chunk - TM / 64 : chunk);
     }
+    // this lane's DMA sources for the tile at w
+    using Offs = DmaOffsets<G::kDmaA, G::kDmaB, G::kDmaPerScales>;
+    auto offsets_of = [&](const TileWhere &w) {
+        Offs o;
+#pragma unroll
+        for (int u = 0; u < G::kDmaA; ++u) {
+            if constexpr (TILED) {
+                const uint32_t rb = (uint32_t)(w.m0 + a_row0 + kRowsPerDma * u) / 16;
+                o.a[u] = rb * kblocks * 1024u + (uint32_t)lane * 16u;
+            } else {
+                const int row = a_row0 + kRowsPerDma * u + lane / 4;
+                const int chunk = (lane % 4) ^ chunk_perm(row);
+                o.a[u] = (uint32_t)(min(w.m0 + row, M - 1) * lda + 16 * chunk);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < G::kDmaB; ++u) {
+            if constexpr (TILED) {
+                const uint32_t rb = (uint32_t)(w.n0 + b_row0 + kRowsPerDma * u) / 16;
+                o.b[u] = rb * kblocks * 1024u + (uint32_t)lane * 16u;
+            } else {
+                const int row = b_row0 + kRowsPerDma * u + lane / 4;
+                const int chunk = (lane % 4) ^ chunk_perm(row);
+                o.b[u] = (uint32_t)(min(w.n0 + row, N - 1) * ldb + 16 * chunk);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < G::kDmaPerScales; ++u) {
+            const int chunk = (wave + NW * u) % G::kScaleChunks;
+            const bool is_b = chunk >= TM / 64;
+            const int q64 = is_b ? chunk - TM / 64 : chunk;
+            const int row = 64 * q64 + lane;
+            o.src[u] = is_b ? w.bs : w.as;
+            if constexpr (TILED) {
+                // 64-row x 512-K scale blocks of 1024 bytes, 16 per row
+                o.s[u] = ((uint32_t)(is_b ? w.n0 : w.m0) / 64 + (uint32_t)q64) * ((uint32_t)K / 512) * 1024u +
+                         (uint32_t)lane * 16u;
+            } else {
+                o.s[u] = (uint32_t)(is_b ? min(w.n0 + row, N - 1) * ldbs : min(w.m0 + row, M - 1) * ldas);
+            }
+        }
+        return o;
+    };
+    Offs offs = offsets_of(cur);
     // fragment and scale reads of this lane
     const int perm = chunk_perm(r);
     const int a_frag = (wm * G::kWaveRows + r) * kRowBytes;
@@ -483,18 +533,21 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
     const int sb_lds = kScaleBase + 16 * (TM + wn * G::kWaveCols + r);
 
     const int stage0 = split * (K / kStageK / splits);  // first stage of this split
+    // stage numbers past the tile's last one (nk + i) mean stage i of the next tile, once the
+    // offsets have been set for it (the persistent walk)
+    int shift = 0;
     auto dma = [&](int buf, int stage) {
-        uint8_t *dst = lds + buf * kStageBytes;
+        uint8_t *dst = lds + kRingBase + buf * kStageBytes;
         const uint32_t step = TILED ? 1024u : (uint32_t)kRowBytes;
-        const uint8_t *asrc = aq + (uint32_t)(stage0 + stage) * step;
-        const uint8_t *bsrc = bq + (uint32_t)(stage0 + stage) * step;
+        const uint8_t *asrc = aq + (uint32_t)(stage0 + stage - shift) * step;
+        const uint8_t *bsrc = bq + (uint32_t)(stage0 + stage - shift) * step;
 #pragma unroll
         for (int u = 0; u < G::kDmaA; ++u)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(asrc + a_off[u]),
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(asrc + offs.a[u]),
                                              (lds_void_t *)(dst + a_row0 * kRowBytes + u * 1024), 16, 0, 0);
 #pragma unroll
         for (int u = 0; u < G::kDmaB; ++u)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(bsrc + b_off[u]),
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(bsrc + offs.b[u]),
                                              (lds_void_t *)(dst + kABytes + b_row0 * kRowBytes + u * 1024), 16, 0,
                                              0);
     };
@@ -502,11 +555,13 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
         uint8_t *dst = lds + kScaleBase + (g & 1) * kScaleSlot;
 #pragma unroll
         for (int u = 0; u < G::kDmaPerScales; ++u)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(s_src[u] + (TILED ? 1024u : 16u) * (uint32_t)(stage0 / 4 + g) + s_off[u]),
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(offs.src[u] + (TILED ? 1024u : 16u) *
+                                                                         (uint32_t)(stage0 / 4 + g - shift / 4) +
+                                                             offs.s[u]),
                                              (lds_void_t *)(dst + s_dst[u]), 16, 0, 0);
     };
     auto read_frags = [&](int buf, int chunk, u32x4 (&fa)[FI], u32x4 (&fb)[FJ]) {
-        const uint8_t *src = lds + buf * kStageBytes;
+        const uint8_t *src = lds + kRingBase + buf * kStageBytes;
 #pragma unroll
         for (int i = 0; i < FI; ++i)
             fa[i] = *reinterpret_cast<const u32x4 *>(src + a_frag + 32 * i * kRowBytes + chunk);
@@ -548,7 +603,7 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
                 mfma_t<decltype(opsel)::value>(acc[i][j], fb[j], fa[i], xb[j], xa[i]);
     };
 
-    const int nk = K / kStageK / splits;  // stages of this split: a multiple of 4, >= 4
+    const int nk = K / kStageK / (PERSIST ? 1 : splits);  // stages of this split: a multiple of 4, >= 4
     const int ngroups = nk / 4;
     u32x4 fa0[FI], fb0[FJ], fa1[FI], fb1[FJ];
     uint32_t sa0[FI], sb0[FJ], sa1[FI], sb1[FJ];
@@ -644,126 +699,204 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
             for (int j = 0; j < FJ; ++j) seg_sum[i][j] = v16f{};
     }
 
-    for (int g = 0; g + 1 < ngroups; ++g) {
-        stage(g, I0(), WS(), T(), T());
-        stage(g, I1(), WSS(), T(), F());
-        stage(g, I2(), WSS(), T(), F());
-        stage(g, I3(), WS(), T(), F());
-        if constexpr (FOLD) {
-            if ((g + 1) % fold_groups == 0) {
+    // the epilogue of the tile at (m0, n0): acc[i][j] register q * 4 + t of lane (r, half) is
+    // C[m0 + kWaveRows wm + 32 i + r][n0 + kWaveCols wn + 32 j + 8 q + 4 half + t]. With split-K
+    // the unscaled partial product goes to partials[split][M][N] (FP32, beta 0) instead.
+    auto epilogue = [&]() {
+        // the lane index passes through an empty asm statement, so that the address arithmetic
+        // below is formed per tile, after the main loop, instead of being hoisted out of the
+        // persistent walk and held in registers through it
+        int lane = tid & 63;
+        if constexpr (PERSIST) asm volatile("" : "+v"(lane));
+        const int r = lane & 31, half = lane >> 5;
+        if (!PERSIST && splits > 1) out = OutSpec{partials + (int64_t)split * M * N, N, 1.0f, 0.0f, 0};
+        float *c = static_cast<float *>(out.c);
+        const int64_t ldc = out.ldc;
+        const float alpha = out.alpha;
+        // split-K partials are FP32 whatever the variant: a bf16 variant decides per launch
+        const bool bf16_now = EPI == kEpiBF16 && out.bf16;
+        const bool full_cols = n0 + TN <= N && (bf16_now ? out_vector_ok<true>(out) : out_vector_ok<false>(out));
+        if (full_cols) {
+            // stage each 32-row slice of this wavefront's kWaveRows x kWaveCols result through LDS
+            // so that a store instruction writes whole rows (64 / (kWaveCols / 4) rows of kWaveCols
+            // floats). Rows are padded by 16 bytes against bank conflicts; in the persistent walk
+            // they are unpadded, their 16-byte chunks XOR-permuted by the row instead.
+            constexpr int kEpiRow = G::kWaveCols * 4 + (PERSIST ? 0 : 16);   // bytes per staged row
+            constexpr int kEpiWave = 32 * kEpiRow;                         // one slice per wavefront
+            constexpr int kLanesPerRow = G::kWaveCols / 4;                 // 16-byte pieces per row
+            constexpr int kRowsPerStore = 64 / kLanesPerRow;
+            static_assert(!PERSIST || kLanesPerRow >= 16, "the chunk permutation spans 16 chunks");
+            const auto at = [](int row, int col_bytes) {
+                return PERSIST ? row * kEpiRow + ((col_bytes >> 4) ^ (row & 15)) * 16 : row * kEpiRow + col_bytes;
+            };
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();                    // every wavefront is done with the stages
+            __builtin_amdgcn_sched_barrier(0);
+            uint8_t *epi = lds + (PERSIST ? kSliceOut : 0) + wave * kEpiWave;
 #pragma unroll
-                for (int i = 0; i < FI; ++i)
+            for (int i = 0; i < FI; ++i) {
 #pragma unroll
-                    for (int j = 0; j < FJ; ++j) {
-                        seg_sum[i][j] = seg_sum[i][j] + acc[i][j];
-                        acc[i][j] = v16f{};
+                for (int jj = 0; jj < FJ; ++jj)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4v v = {acc[i][jj][4 * q + 0], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
+                                          acc[i][jj][4 * q + 3]};
+                        *reinterpret_cast<f32x4v *>(epi + at(r, (32 * jj + 8 * q + 4 * half) * 4)) = v;
                     }
+                constexpr int kStores = 32 / kRowsPerStore;
+                const int cc = 4 * (lane % kLanesPerRow);
+                const int64_t ncol = n0 + wn * G::kWaveCols + cc;
+                if constexpr (EPI == kEpiF32) {
+#pragma unroll
+                    for (int p = 0; p < kStores; ++p) {
+                        const int rr = kRowsPerStore * p + lane / kLanesPerRow;
+                        f32x4v v = *reinterpret_cast<const f32x4v *>(epi + at(rr, cc * 4));
+                        v = v * alpha;
+                        const int m = m0 + wm * G::kWaveRows + 32 * i + rr;
+                        if (m < M) *reinterpret_cast<f32x4v *>(c + (int64_t)m * ldc + ncol) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int p = 0; p < kStores; ++p) {
+                        const int rr = kRowsPerStore * p + lane / kLanesPerRow;
+                        f32x4v v = *reinterpret_cast<const f32x4v *>(epi + at(rr, cc * 4));
+                        v = v * alpha;
+                        const int m = m0 + wm * G::kWaveRows + 32 * i + rr;
+                        if (m < M) {
+                            if (bf16_now)
+                                store4<true>(out, m, ncol, N, v, true);
+                            else
+                                store4<false>(out, m, ncol, N, v, true);
+                        }
+                    }
+                }
             }
+            return;
         }
-    }
-    {
-        const int g = ngroups - 1;
-        stage(g, I0(), WS(), T(), F());
-        stage(g, I1(), WS(), F(), F());
-        stage(g, I2(), W0(), F(), F());
-        stage(g, I3(), WNone(), F(), F());
-    }
-    if constexpr (FOLD) {
-        // the last segment joins the earlier ones
-#pragma unroll
-        for (int i = 0; i < FI; ++i)
-#pragma unroll
-            for (int j = 0; j < FJ; ++j) acc[i][j] = seg_sum[i][j] + acc[i][j];
-    }
-
-    // epilogue: acc[i][j] register q * 4 + t of lane (r, half) is
-    // C[m0 + kWaveRows wm + 32 i + r][n0 + kWaveCols wn + 32 j + 8 q + 4 half + t]. With split-K the
-    // unscaled partial product goes to partials[split][M][N] (FP32, beta 0) instead.
-    if (splits > 1) out = OutSpec{partials + (int64_t)split * M * N, N, 1.0f, 0.0f, 0};
-    float *c = static_cast<float *>(out.c);
-    const int64_t ldc = out.ldc;
-    const float alpha = out.alpha;
-    // split-K partials are FP32 whatever the variant: a bf16 variant decides per launch
-    const bool bf16_now = EPI == kEpiBF16 && out.bf16;
-    const bool full_cols = n0 + TN <= N && (bf16_now ? out_vector_ok<true>(out) : out_vector_ok<false>(out));
-    if (full_cols) {
-        // stage each 32-row slice of this wavefront's kWaveRows x kWaveCols result through LDS so
-        // that a store instruction writes whole rows (64 / (kWaveCols / 4) rows of kWaveCols floats)
-        constexpr int kEpiRow = G::kWaveCols * 4 + 16;   // bytes per staged row (padded)
-        constexpr int kEpiWave = 32 * kEpiRow;           // one slice per wavefront
-        constexpr int kLanesPerRow = G::kWaveCols / 4;   // 16-byte pieces per row
-        constexpr int kRowsPerStore = 64 / kLanesPerRow;
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();                    // every wavefront is done with the stages
-        __builtin_amdgcn_sched_barrier(0);
-        uint8_t *epi = lds + wave * kEpiWave;
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
+            const int m = m0 + wm * G::kWaveRows + 32 * i + r;
+            if (m >= M) continue;
+            float *crow = c + (int64_t)m * ldc;
 #pragma unroll
             for (int jj = 0; jj < FJ; ++jj)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4v v = {acc[i][jj][4 * q + 0], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
-                                      acc[i][jj][4 * q + 3]};
-                    *reinterpret_cast<f32x4v *>(epi + r * kEpiRow + (32 * jj + 8 * q + 4 * half) * 4) = v;
-                }
-            constexpr int kStores = 32 / kRowsPerStore;
-            const int cc = 4 * (lane % kLanesPerRow);
-            const int64_t ncol = n0 + wn * G::kWaveCols + cc;
-            if constexpr (EPI == kEpiF32) {
-#pragma unroll
-                for (int p = 0; p < kStores; ++p) {
-                    const int rr = kRowsPerStore * p + lane / kLanesPerRow;
-                    f32x4v v = *reinterpret_cast<const f32x4v *>(epi + rr * kEpiRow + cc * 4);
-                    v = v * alpha;
-                    const int m = m0 + wm * G::kWaveRows + 32 * i + rr;
-                    if (m < M) *reinterpret_cast<f32x4v *>(c + (int64_t)m * ldc + ncol) = v;
-                }
-            } else {
-#pragma unroll
-                for (int p = 0; p < kStores; ++p) {
-                    const int rr = kRowsPerStore * p + lane / kLanesPerRow;
-                    f32x4v v = *reinterpret_cast<const f32x4v *>(epi + rr * kEpiRow + cc * 4);
-                    v = v * alpha;
-                    const int m = m0 + wm * G::kWaveRows + 32 * i + rr;
-                    if (m < M) {
+                    const int n = n0 + wn * G::kWaveCols + 32 * jj + 8 * q + 4 * half;
+                    const f32x4v v = {alpha * acc[i][jj][4 * q + 0], alpha * acc[i][jj][4 * q + 1],
+                                      alpha * acc[i][jj][4 * q + 2], alpha * acc[i][jj][4 * q + 3]};
+                    if constexpr (EPI == kEpiBF16) {
                         if (bf16_now)
-                            store4<true>(out, m, ncol, N, v, true);
+                            store4<true>(out, m, n, N, v, false);
                         else
-                            store4<false>(out, m, ncol, N, v, true);
+                            store4<false>(out, m, n, N, v, false);
+                    } else if constexpr (EPI == kEpiF32Beta) {
+                        store4<false>(out, m, n, N, v, false);
+                    } else if (full_cols) {
+                        *reinterpret_cast<f32x4v *>(crow + n) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) crow[n + e] = v[e];
                     }
+                }
+        }
+    };
+
+    // virtual blocks of the launch (the persistent walk's range)
+    const int nblocks = GROUP ? total * grp.count : total * splits;
+    for (;;) {
+        // the next tile of the walk (after the last one: this tile again), located now, while the
+        // registers of the last stages are not yet needed
+        bool has_next = false;
+        TileWhere next{};
+        Offs next_offs{};
+        if constexpr (PERSIST) {
+            has_next = vblock + (int)gridDim.x < nblocks;
+            next = locate(has_next ? vblock + (int)gridDim.x : vblock);
+            next_offs = offsets_of(next);
+            // formed here (empty asm statements): left to the scheduler, the arithmetic sinks into
+            // the last stages, where the fragments already hold most registers
+#pragma unroll
+            for (int u = 0; u < G::kDmaA; ++u) asm volatile("" : "+v"(next_offs.a[u]));
+#pragma unroll
+            for (int u = 0; u < G::kDmaB; ++u) asm volatile("" : "+v"(next_offs.b[u]));
+#pragma unroll
+            for (int u = 0; u < G::kDmaPerScales; ++u) asm volatile("" : "+v"(next_offs.s[u]));
+        }
+        for (int g = 0; g + 1 < ngroups; ++g) {
+            stage(g, I0(), WS(), T(), T());
+            stage(g, I1(), WSS(), T(), F());
+            stage(g, I2(), WSS(), T(), F());
+            stage(g, I3(), WS(), T(), F());
+            if constexpr (FOLD) {
+                if ((g + 1) % fold_groups == 0) {
+#pragma unroll
+                    for (int i = 0; i < FI; ++i)
+#pragma unroll
+                        for (int j = 0; j < FJ; ++j) {
+                            seg_sum[i][j] = seg_sum[i][j] + acc[i][j];
+                            acc[i][j] = v16f{};
+                        }
                 }
             }
         }
-        return;
-    }
+        const int g = ngroups - 1;
+        if constexpr (PERSIST) {
+            stage(g, I0(), WS(), T(), F());
+            // every load of this tile is issued: the DMA now brings the next tile's stages 0 and 1
+            // (as stages nk and nk + 1, into ring buffers 0 and 1) and its group-0 scales (slot 0,
+            // free since the number of groups is even). After the last tile the same loads bring
+            // this tile's first stages again, unused, so that one code path serves both.
+            offs = next_offs;
+            aq = next.aq;
+            bq = next.bq;
+            shift = nk;
+            stage(g, I1(), WS(), T(), T());
+            stage(g, I2(), WSS(), T(), F());
+            stage(g, I3(), WNone(), F(), F());
+        } else {
+            stage(g, I0(), WS(), T(), F());
+            stage(g, I1(), WS(), F(), F());
+            stage(g, I2(), W0(), F(), F());
+            stage(g, I3(), WNone(), F(), F());
+        }
+        if constexpr (FOLD) {
+            // the last segment joins the earlier ones
 #pragma unroll
-    for (int i = 0; i < FI; ++i) {
-        const int m = m0 + wm * G::kWaveRows + 32 * i + r;
-        if (m >= M) continue;
-        float *crow = c + (int64_t)m * ldc;
+            for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < FJ; ++jj)
+                for (int j = 0; j < FJ; ++j) acc[i][j] = seg_sum[i][j] + acc[i][j];
+        }
+        // the walk: the next tile's first stages and scales land before any store is issued, so
+        // that nothing waits for the stores to drain until the next tile's first stage
+        if constexpr (PERSIST) wait_vmcnt<0>();
+        epilogue();
+        if (!has_next) return;
+
+        // the next tile: its stages 0 and 1 and scales landed before this wavefront's first store
+        // (vmcnt 0 above), every wavefront's once all have passed the barrier, which also ends the
+        // staged epilogue's reads of ring buffers 2 and 3. The stores drain meanwhile: the first
+        // stage's wait counts them too.
+        vblock += (int)gridDim.x;
+        split = next.split;
+        m0 = next.m0;
+        n0 = next.n0;
+        out.c = next.c;
+        shift = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * G::kWaveCols + 32 * jj + 8 * q + 4 * half;
-                const f32x4v v = {alpha * acc[i][jj][4 * q + 0], alpha * acc[i][jj][4 * q + 1],
-                                  alpha * acc[i][jj][4 * q + 2], alpha * acc[i][jj][4 * q + 3]};
-                if constexpr (EPI == kEpiBF16) {
-                    if (bf16_now)
-                        store4<true>(out, m, n, N, v, false);
-                    else
-                        store4<false>(out, m, n, N, v, false);
-                } else if constexpr (EPI == kEpiF32Beta) {
-                    store4<false>(out, m, n, N, v, false);
-                } else if (full_cols) {
-                    *reinterpret_cast<f32x4v *>(crow + n) = v;
-                } else {
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) crow[n + e] = v[e];
-                }
+            for (int j = 0; j < FJ; ++j) {
+                acc[i][j] = v16f{};
+                if constexpr (FOLD) seg_sum[i][j] = v16f{};
             }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        dma(2, 2);
+        read_frags(0, chunk0, fa0, fb0);
+        read_scales(0, sa0, sb0);
     }
 }
 
@@ -813,6 +946,11 @@ int gemm_splits(int64_t M, int64_t N, int64_t K)
     if (s > 1 && K / 32 / s + s > kMaxDepth) return 1;
     return s;
 }
+
+// the persistent walk (256 x 256 tiles, and the 256 x 128 tiles of segmented chains): more
+// tiles than CUs, and an even number of 512-wide groups per contraction (the next tile's first
+// scales go to the slot the last group leaves free)
+static bool persistent_ok(int64_t tiles, int64_t K) { return tiles > kComputeUnits && K % 1024 == 0; }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
@@ -871,6 +1009,17 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
     if (splits == 1 && fold > 0 && tiles_m * tiles_n > kComputeUnits / 2) {
         // segmented chains on a full grid: the 256 x 128 tile
         const int mm = (int)((M + kFoldTM - 1) / kFoldTM), mn = (int)((N + kFoldTN - 1) / kFoldTN);
+        if (epi == kEpiF32 && persistent_ok(mm * mn, K)) {
+            const auto run_walk = [&](auto kernel) {
+                return launch(kernel, dim3(kComputeUnits), dim3(64 * kFoldWaves), 0, stream, aq, lda, as, ldas, bq,
+                              ldb, bs, ldbs, (int)M, (int)N, (int)K, out, mm, mn, 1, (float *)nullptr, fold,
+                              GroupArgs{});
+            };
+            return tiled ? run_walk(gemm_mxfp4_pipelined<kFoldWaves, true, kEpiF32, kFoldTM, kFoldTN, 4, true, false,
+                                                         true>)
+                         : run_walk(gemm_mxfp4_pipelined<kFoldWaves, false, kEpiF32, kFoldTM, kFoldTN, 4, true, false,
+                                                         true>);
+        }
         const auto run_mid = [&](auto kernel) {
             return launch(kernel, dim3((unsigned)(mm * mn)), dim3(64 * kFoldWaves), 0, stream, aq, lda, as, ldas, bq,
                           ldb, bs, ldbs, (int)M, (int)N, (int)K, out, mm, mn, 1, (float *)nullptr, fold,
@@ -892,6 +1041,16 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
         };
         if (fold > 0) return pick(run_small, C4(), C128(), C128(), C2(), std::true_type());
         return pick(run_small, C4(), C128(), C128(), C2(), std::false_type());
+    }
+    if (splits == 1 && epi == kEpiF32 && persistent_ok(tiles_m * tiles_n, K)) {
+        // more tiles than CUs: one workgroup per CU walks them
+        const auto run_walk = [&](auto kernel) {
+            return launch(kernel, dim3(kComputeUnits), dim3(64 * kGemmWaves), 0, stream, aq, lda, as, ldas, bq, ldb,
+                          bs, ldbs, (int)M, (int)N, (int)K, out, tiles_m, tiles_n, 1, (float *)nullptr, 0,
+                          GroupArgs{});
+        };
+        return tiled ? run_walk(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32, kBM, kBN, 2, false, false, true>)
+                     : run_walk(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiF32, kBM, kBN, 2, false, false, true>);
     }
     const dim3 grid((unsigned)(tiles_m * tiles_n * splits)), block(64 * kGemmWaves);
     const auto run = [&](auto kernel) {
@@ -949,17 +1108,38 @@ hipError_t launch_gemm_grouped(const GemmGroupItem *items, int count, int64_t ld
                       items[0].as, ldas, items[0].bq, ldb, items[0].bs, ldbs, (int)M, (int)N, (int)K, out, gm, gn, 1,
                       (float *)nullptr, fold, grp);
     };
-    if (fold > 0 && big_tiles > kComputeUnits / 2)
+    // the walk over all the products' tiles of geometry tm x tn, one workgroup per CU
+    auto run_walk = [&](auto kernel, int nw, int tm, int tn) {
+        const int gm = (int)((M + tm - 1) / tm), gn = (int)((N + tn - 1) / tn);
+        return launch(kernel, dim3(kComputeUnits), dim3(64 * nw), 0, stream, items[0].aq, lda, items[0].as, ldas,
+                      items[0].bq, ldb, items[0].bs, ldbs, (int)M, (int)N, (int)K, out, gm, gn, 1, (float *)nullptr,
+                      fold, grp);
+    };
+    if (fold > 0 && big_tiles > kComputeUnits / 2) {
+        const int64_t fold_tiles = ((M + kFoldTM - 1) / kFoldTM) * ((N + kFoldTN - 1) / kFoldTN) * count;
+        if (persistent_ok(fold_tiles, K))
+            return tiled ? run_walk(gemm_mxfp4_pipelined<kFoldWaves, true, kEpiF32, kFoldTM, kFoldTN, 4, true, true,
+                                                         true>,
+                                    kFoldWaves, kFoldTM, kFoldTN)
+                         : run_walk(gemm_mxfp4_pipelined<kFoldWaves, false, kEpiF32, kFoldTM, kFoldTN, 4, true, true,
+                                                         true>,
+                                    kFoldWaves, kFoldTM, kFoldTN);
         return tiled ? run(gemm_mxfp4_pipelined<kFoldWaves, true, kEpiF32, kFoldTM, kFoldTN, 4, true, true>,
                            kFoldWaves, kFoldTM, kFoldTN)
                      : run(gemm_mxfp4_pipelined<kFoldWaves, false, kEpiF32, kFoldTM, kFoldTN, 4, true, true>,
                            kFoldWaves, kFoldTM, kFoldTN);
+    }
     if (fold > 0)
         return tiled ? run(gemm_mxfp4_pipelined<4, true, kEpiF32, 128, 128, 2, true, true>, 4, 128, 128)
                      : run(gemm_mxfp4_pipelined<4, false, kEpiF32, 128, 128, 2, true, true>, 4, 128, 128);
     if (big_tiles <= kComputeUnits / 2)
         return tiled ? run(gemm_mxfp4_pipelined<4, true, kEpiF32, 128, 128, 2, false, true>, 4, 128, 128)
                      : run(gemm_mxfp4_pipelined<4, false, kEpiF32, 128, 128, 2, false, true>, 4, 128, 128);
+    if (persistent_ok(big_tiles, K))
+        return tiled ? run_walk(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32, kBM, kBN, 2, false, true, true>,
+                                kGemmWaves, kBM, kBN)
+                     : run_walk(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiF32, kBM, kBN, 2, false, true, true>,
+                                kGemmWaves, kBM, kBN);
     return tiled ? run(gemm_mxfp4_pipelined<kGemmWaves, true, kEpiF32, kBM, kBN, 2, false, true>, kGemmWaves, kBM, kBN)
                  : run(gemm_mxfp4_pipelined<kGemmWaves, false, kEpiF32, kBM, kBN, 2, false, true>, kGemmWaves, kBM, kBN);
 }
