@@ -55,6 +55,8 @@ def _sample(rng, M, N, count):
     (4352, 3856, 2048, "tiled", True),     # 17 x 16 = 272 tiles
     (8192, 4096, 4096, "tiled", False),    # the q / o projection's Fprop over 8192 tokens: 2 rounds
     (8192, 14336, 4096, "tiled", False),   # the gate Fprop: 7 rounds
+    (65792, 256, 1024, "tiled", False),    # 257 x 1 tiles: one workgroup takes two, no XCD spread
+    (200, 76800, 2048, "rows", False),     # 1 x 300 tiles, 200 of 256 rows
     (8192, 4096, 1024, "rows", False),     # the k / v Dgrad shape: 2 groups per contraction
     (4400, 4000, 1536, "tiled", True),     # 3 groups: one workgroup per tile instead
     (4096, 4096, 8192, "tiled", False),    # segmented chains: the q projection's Wgrad, 512 tiles
