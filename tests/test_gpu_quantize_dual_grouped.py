@@ -73,3 +73,22 @@ def test_grouped_tensor_without_tiles():
     for x, g in ((a, got[0]), (b, got[2])):
         ref = mx.quantize_dual(x, 16)
         assert all(np.array_equal(host(u), host(v)) for u, v in zip(g, ref))
+
+
+def test_grouped_eight_tensors_randomized_and_orthonormal():
+    """The largest group (8 tensors of different shapes, bf16 in one launch and f32 in another)
+    with the randomized Hadamard and with the orthonormal rotation: the same bytes as eight
+    separate launches."""
+    import mxfp4_block_scaled_h16_amd as mx
+    rng = np.random.default_rng(23)
+    shapes = [(256, 512), (96, 160), (512, 256), (64, 1024), (1024, 64), (160, 96), (320, 640), (32, 32)]
+    opts = [(dict(seed=31 + i), dict(rounding="sr", seed=41 + i, stream_id=i)) for i in range(len(shapes))]
+    for f32 in (False, True):
+        xs = [_tensor(rng, r, c, f32) for r, c in shapes]
+        for h in (16 | mx.RHT, 32 | mx.ORTHO):
+            announce("dual grouped eight tensors f32", f32, "h", h)
+            got = mx.quantize_dual_grouped([(x, *o) for x, o in zip(xs, opts)], h)
+            for i, (x, o) in enumerate(zip(xs, opts)):
+                ref = mx.quantize_dual(x, h, *o)
+                for k, (u, v) in enumerate(zip(got[i], ref)):
+                    assert np.array_equal(host(u), host(v)), "tensor %d output %d, h %d" % (i, k, h)
