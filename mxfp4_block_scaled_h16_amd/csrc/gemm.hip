@@ -1006,8 +1006,10 @@ hipError_t launch_gemm(const uint8_t *aq, int64_t lda, const uint8_t *as, int64_
     using C2 = std::integral_constant<int, 2>;
     using C128 = std::integral_constant<int, 128>;
     using C256 = std::integral_constant<int, 256>;
-    if (splits == 1 && fold > 0 && tiles_m * tiles_n > kComputeUnits / 2) {
-        // segmented chains on a full grid: the 256 x 128 tile
+    if (splits == 1 && fold > 0 && tiles_m * tiles_n >= kComputeUnits / 2) {
+        // segmented chains on a full grid (from 128 large tiles, i.e. 256 of these: one per CU,
+        // measured 2-3% faster than 512 of 128 x 128 at 1024 x 4096 x 8192 and 4096 x 2048 x
+        // 14336): the 256 x 128 tile
         const int mm = (int)((M + kFoldTM - 1) / kFoldTM), mn = (int)((N + kFoldTN - 1) / kFoldTN);
         if (epi == kEpiF32 && persistent_ok(mm * mn, K)) {
             const auto run_walk = [&](auto kernel) {
@@ -1115,7 +1117,7 @@ hipError_t launch_gemm_grouped(const GemmGroupItem *items, int count, int64_t ld
                       items[0].bq, ldb, items[0].bs, ldbs, (int)M, (int)N, (int)K, out, gm, gn, 1, (float *)nullptr,
                       fold, grp);
     };
-    if (fold > 0 && big_tiles > kComputeUnits / 2) {
+    if (fold > 0 && big_tiles >= kComputeUnits / 2) {   // as in launch_gemm
         const int64_t fold_tiles = ((M + kFoldTM - 1) / kFoldTM) * ((N + kFoldTN - 1) / kFoldTN) * count;
         if (persistent_ok(fold_tiles, K))
             return tiled ? run_walk(gemm_mxfp4_pipelined<kFoldWaves, true, kEpiF32, kFoldTM, kFoldTN, 4, true, true,
