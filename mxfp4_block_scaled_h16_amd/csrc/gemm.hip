@@ -405,13 +405,14 @@ __global__ __launch_bounds__(64 * NW, (Geo<NW, TM, TN, WM>::kMinBlocks)) void ge
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
     // tile order: consecutive workgroups are spread over the 8 XCDs; give each XCD a contiguous
-    // range of tiles, walked column-panel by column-panel in groups of row panels, so that one
-    // round of an XCD's 32 CUs covers about a square region and its operand panels are shared
-    // through that XCD's L2: 8 row panels of 256 x 256 tiles, 4 of 256 x 128 tiles (4 x 8 tiles
-    // fetch 20% fewer operand bytes per round than 8 x 4; measured 1-1.5% faster on the
-    // segmented-chain products of the decoder layer, 4.025 -> 4.006 ms per step)
+    // range of tiles, walked column-panel by column-panel in groups of row panels covering 1024
+    // rows of A, so that one round of an XCD's 32 CUs shares its operand panels through that
+    // XCD's L2: 4 row panels x 8 column panels of 256 x 128 tiles (20% fewer operand bytes per
+    // round than 8 x 4; 1-1.5% faster on the segmented-chain products of the decoder layer), and
+    // 4 x 8 of 256 x 256 tiles too (with the tile walk, 2-5% faster than 8 x 4 on the layer's
+    // 256 x 256 products in two same-session A/Bs, 16 x 2 slower)
     const int total = tiles_m * tiles_n;
-    constexpr int kGroupRows = 8 * TN / TM;   // a round of 32 tiles covers about a square region
+    constexpr int kGroupRows = 1024 / TM;
     // virtual block v: its K-split, tile origin and (grouped) the product's operands and output
     auto locate = [&](int v) {
         TileWhere w;
