@@ -294,7 +294,7 @@ typedef struct {
  *   count    0 .. MXFP4_GEMM_GROUP_MAX (0: nothing to do).
  * M, N, K, the leading dimensions, alpha and the layout apply to every item, with mxfp4_gemm's
  * requirements. No workspace: the contraction is never split. Row-major operands whose K is not
- * a multiple of 512 run one launch per item.
+ * a multiple of 512 take the row kernel, one grid layer per item, still in one launch.
  * Errors: MXFP4_ERR_ARG for count out of range or overlapping outputs; otherwise those of
  * mxfp4_gemm, for the first item that fails them (nothing is launched then).
  */

@@ -69,8 +69,9 @@ int gemm_splits(int64_t M, int64_t N, int64_t K);
 
 // Several products of the same shape, strides and layout in one launch (FP32 output, alpha,
 // beta 0, no split of K): one grid over all their tiles, so that products with few tiles fill
-// the chip together. Falls back to one launch per product where the pipelined kernel does not
-// apply (K % 512 != 0 row-major operands) or for more than 8 products.
+// the chip together. Where the pipelined kernel does not apply (K % 512 != 0 row-major
+// operands) the row kernel runs them as the layers of a three-dimensional grid; more than 8
+// products fall back to one launch each.
 struct GemmGroupItem {
     const uint8_t *aq, *as, *bq, *bs;
     float *c;
