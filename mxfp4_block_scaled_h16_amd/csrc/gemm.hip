@@ -282,7 +282,11 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_simple(
 //  * the epilogue stages each wavefront's result through LDS in 32-row slices, so that every
 //    store instruction writes whole row segments (whole 128-byte lines) instead of 32-byte
 //    pieces of 32 rows: the FP32 output is the largest HBM stream of the kernel and its writes
-//    all come at once, when every CU finishes its tile.
+//    all come at once, when every CU finishes its tile;
+//  * with more tiles than CUs, one workgroup per CU walks them (the PERSIST form below): the
+//    next tile's first two stages and scales are loaded during the current tile's last stages,
+//    so a CU's later tiles start without a prologue and its stores drain during the next
+//    tile's first stage.
 // Rows of a stage buffer hold their four 16-byte chunks XOR-permuted by bits 2-3 of the row: the
 // LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, 64 banks) at a time, and the 16 rows
 // those lanes read then land in 16 distinct bank groups.
