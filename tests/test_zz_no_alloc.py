@@ -40,9 +40,11 @@ def test_noalloc_fprop_matches_the_workspace_call_twice(h, rnd):
     mx, L = _lib()
     r = mx._rounding(rnd)
     cfg = mx.LinearCfg(h, r, r, 0x5EED)
-    # the first product uses the tiled layout and a split K (few output tiles); the second is
-    # smaller, row-major (K not a multiple of 512) and runs after the first in the same array
-    for M, K, N, seed in ((512, 4096, 768, 1), (160, 224, 96, 2)):
+    # the first product is the QKV projection's Fprop over 8192 tokens (768 output tiles: one
+    # workgroup per CU walks them; 31 MB of quantized operands in the array); the second uses the
+    # tiled layout and a split K (few output tiles); the third is smaller, row-major (K not a
+    # multiple of 512); each runs after the previous one in the same array
+    for M, K, N, seed in ((8192, 4096, 6144, 3), (512, 4096, 768, 1), (160, 224, 96, 2)):
         x, w, _ = inputs.linear_inputs(M, K, N, seed=seed)
         xd, wd = bf16_dev(x), bf16_dev(w)
         announce("noalloc fprop", M, K, N, "h", h, rnd)
